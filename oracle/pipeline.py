@@ -1,0 +1,60 @@
+"""The whole Ulysses group run through the C oracle, rank by rank.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The stats all-gather is the stack of every rank's boundary min/max, and the all-to-all is
+the regrouping of the per-rank send buffers by destination (unpack_for_sage Parameters:
+the receive buffer is source-major [world_size, chunk_bytes]).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (boundary_minmax, derive_k_boundary_amax, k_grouped_amax, pack,
+               unpack_for_sage)
+
+
+def shards(X: torch.Tensor, world_size: int):
+    """Global [B,S,H,D] -> list of contiguous rank shards [B,L,H,D]."""
+    B, S, H, D = X.shape
+    L = S // world_size
+    return [X[:, r * L:(r + 1) * L].contiguous() for r in range(world_size)]
+
+
+def run_group(Q, K, V, mean, *, world_size, used_sequence=None, scale_sequence=None,
+              destinations=None, _lib=None):
+    """Q, K, V: global [B,S,H,D]; mean [B,H,D].  Returns every intermediate:
+    q_minmax/k_minmax [P,B,H,2,2,D], q_amax_kernel/k_amax_kernel (before derive) and
+    q_amax/k_amax (after derive) per rank, send buffers per rank, and the unpack 5-tuple
+    per destination (all destinations unless ``destinations`` lists a subset)."""
+    P = world_size
+    B, S, H, D = Q.shape
+    L = S // P
+    kw = dict(world_size=P, _lib=_lib)
+    qs, ks, vs = shards(Q, P), shards(K, P), shards(V, P)
+    q_mm = torch.stack([boundary_minmax(qs[r], rank=r, used_sequence=used_sequence, **kw)
+                        for r in range(P)])
+    k_mm = torch.stack([boundary_minmax(ks[r], rank=r, used_sequence=used_sequence, **kw)
+                        for r in range(P)])
+    q_amax_kernel = [k_grouped_amax(qs[r], None, rank=r, used_sequence=used_sequence, **kw)
+                     for r in range(P)]
+    k_amax_kernel = [k_grouped_amax(ks[r], mean, rank=r, used_sequence=used_sequence, **kw)
+                     for r in range(P)]
+    q_amax = [a.clone() for a in q_amax_kernel]
+    k_amax = [a.clone() for a in k_amax_kernel]
+    for r in range(P):
+        derive_k_boundary_amax(q_amax[r], q_mm, None, rank=r, local_sequence=L,
+                               dtype=Q.dtype, **kw)
+        derive_k_boundary_amax(k_amax[r], k_mm, mean, rank=r, local_sequence=L, **kw)
+    sends = [pack(qs[r], ks[r], vs[r], mean, q_amax[r], k_amax[r], rank=r, **kw)
+             for r in range(P)]
+    dests = range(P) if destinations is None else destinations
+    outs = {}
+    for p in dests:
+        recv = torch.stack([sends[r][p] for r in range(P)])
+        outs[p] = unpack_for_sage(recv, batch_size=B, local_sequence=L, local_heads=H // P,
+                                  head_dim=D, world_size=P, scale_sequence=scale_sequence,
+                                  _lib=_lib)
+    return dict(q_minmax=q_mm, k_minmax=k_mm, q_amax_kernel=q_amax_kernel,
+                k_amax_kernel=k_amax_kernel, q_amax=q_amax, k_amax=k_amax, sends=sends,
+                outs=outs)

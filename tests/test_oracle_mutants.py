@@ -1,0 +1,121 @@
+"""The pins must catch plausible mistakes in the oracle (CPU only).
+
+Each mutant is oracle.c with one deliberate slip (a dropped term, a flipped sign, a wrong
+index or bound).  It is compiled into a temporary library, swapped in for the real oracle,
+and the pin tests are run against it: at least one must fail.  The real oracle source is
+never modified.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import test_oracle_pins as pins
+import test_oracle_pipeline as pipe
+from helpers import small
+
+MUTANTS = {
+    "centering_sign": ("float c = fabsf(v - m);", "float c = fabsf(v + m);"),
+    "floor_dropped": ("out[(b * H + hh) * slots + j] = fmaxf(ORA_FLOOR, amax);",
+                      "out[(b * H + hh) * slots + j] = amax;"),
+    "used_fix_dropped": ("if (u < S && g == partial_live && hi > u) hi = u;", ""),
+    "minmax_includes_padding": ("        if (hi > u) hi = u;\n", "\n"),
+    "derive_min_side_sign": ("c = fmaxf(c, fmaxf(mx - m, m - mn));",
+                             "c = fmaxf(c, fmaxf(mx - m, mn - m));"),
+    "derive_min_side_dropped": ("c = fmaxf(c, fmaxf(mx - m, m - mn));",
+                                "c = fmaxf(c, mx - m);"),
+    "derive_toucher_off_by_one": ("lo < ORA_GROUP * g + ORA_GROUP && ORA_GROUP * g < hi",
+                                  "lo <= ORA_GROUP * g + ORA_GROUP && ORA_GROUP * g <= hi"),
+    "derive_boundary_index_swapped": ("int er = (g == first_group(r, L)) ? 0 : 1;",
+                                      "int er = (g == first_group(r, L)) ? 1 : 0;"),
+    "scale_divisor": ("q_amax[(b * H + hh) * slots + sl] / 127.0f",
+                      "q_amax[(b * H + hh) * slots + sl] / 128.0f"),
+    "clamp_bound": ("if (q < -127.0f) q = -127.0f;", "if (q < -128.0f) q = -128.0f;"),
+    "round_half_away": ("float q = rintf(x / scale);", "float q = roundf(x / scale);"),
+    "shard_grid_slot": ("int64_t sl = (rank * L + l) / ORA_GROUP - g0;",
+                        "int64_t sl = l / ORA_GROUP;"),
+    "pack_head_index": ("int64_t dst = ((b * L + l) * h + j) * D + d;",
+                        "int64_t dst = ((b * h + j) * L + l) * D + d;"),
+    "e4m3_truncates": ("float n = rintf(ldexpf(a, 3 - E));",
+                       "float n = floorf(ldexpf(a, 3 - E));"),
+    "e4m3_saturates_to_nan": ("if (a >= 448.0f) return sign | 0x7E;",
+                              "if (a >= 448.0f) return sign | 0x7F;"),
+    "e4m3_subnormal_step": ("float n = rintf(ldexpf(a, 9));", "float n = rintf(ldexpf(a, 8));"),
+    "fp16_subnormal_exponent": ("mag = ldexpf((float)m, -24);", "mag = ldexpf((float)m, -25);"),
+    "unpack_scale_source": ("int64_t s = ORA_GROUP * g / L;",
+                            "int64_t s = (ORA_GROUP * g + ORA_GROUP - 1) / L;"),
+    "unpack_v_tail": ("uint8_t vb = 0;", "uint8_t vb = 1;"),
+    "unpack_v_transpose": ("v8[((b * D + d) * h + j) * spad + t] = vb;",
+                           "v8[((b * h + j) * D + d) * spad + t] = vb;"),
+    "slots_formula": ("(L + ORA_GROUP - 1) / ORA_GROUP + 1", "(L + ORA_GROUP - 1) / ORA_GROUP"),
+}
+
+
+def battery():
+    """A quick subset of the pin tests.  Returns the names of those that failed."""
+    failed = []
+    checks = [
+        ("e4m3_table", lambda: pins.test_e4m3_ocp_table(None)),
+        ("e4m3_exhaustive_bf16",
+         lambda: pins.test_e4m3_exhaustive_vs_brute_force_and_torch(None, torch.bfloat16)),
+        ("quant_ties", lambda: pins.test_quant_i8_ties_go_to_even(None)),
+        ("decode_fp16", lambda: pins.test_input_decoding_matches_library(None, torch.float16)),
+        ("worked_example", lambda: pipe.test_hand_worked_example(None)),
+        ("padding_only", lambda: pipe.test_padding_only_slice_contributes_floor(None)),
+        ("only_partial_live", lambda: pipe.test_only_partial_live_group_changes(None, 195)),
+    ]
+    for w in [small(B=2, P=4, L=100, H=8, D=64, used=301, scale_sequence=301, seed=1),
+              small(P=2, L=65, H=4, D=128, dtype=torch.float16, used=100, seed=2),
+              small(P=6, L=31, H=6, D=64, used=150, seed=3),
+              small(P=8, L=200, H=8, D=64, seed=4),
+              small(P=4, L=128, H=4, D=64, used=400, seed=5)]:
+        checks.append((f"definition_{w.name}", lambda w=w: pipe.test_pipeline_matches_definition(
+            None, w)))
+    for name, fn in checks:
+        try:
+            fn()
+        except (AssertionError, ValueError, RuntimeError, IndexError):
+            failed.append(name)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def source():
+    return open(oracle.SRC_PATH).read()
+
+
+def test_real_oracle_passes_battery(olib):
+    assert battery() == []
+
+
+def _run_battery_with(lib_path: str) -> int:
+    """Child process entry: swap in the library at lib_path, run the battery.  Exit 0 when
+    a pin failed (mutant caught), 3 when every pin passed."""
+    oracle._lib = oracle.lib(lib_path)
+    failed = battery()
+    print("failed pins:", failed)
+    return 0 if failed else 3
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(olib, source, tmp_path, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) >= 1, f"mutation site for {name} not found"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new, 1))
+    so = oracle.build(out=str(tmp_path / "libmutant.so"), src=str(src))
+    # a mutant may write out of bounds: run it in a child process; a crash also counts as
+    # caught, since the pin run could not complete
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = ("import sys; sys.path[:0] = [%r, %r]; import test_oracle_mutants as m; "
+            "sys.exit(m._run_battery_with(%r))" % (here, os.path.dirname(here), so))
+    proc = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                          timeout=600)
+    assert proc.returncode != 3, f"mutant {name} passed every pin"
+    assert proc.returncode == 0 or proc.returncode < 0, proc.stderr[-2000:]
