@@ -1,0 +1,232 @@
+"""Benchmark of the smooth-K low-precision Ulysses pack/unpack on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input held in HBM:
+fused Q/K statistics (grouped amax + boundary min/max, every rank), the boundary derive,
+the pack of every rank into the all-to-all buffer, and the unpack of every destination --
+four launches on one stream.  Inputs and outputs rotate over several buffer sets so that
+each step reads data last touched several steps earlier (the sets together exceed the
+256 MB last-level cache).
+
+The reported value is pack+unpack algorithmic bytes / pack+unpack kernel time (HIP events
+around those launches in every timed step); the statistics kernel is reported beside it
+(amax GB/s).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["precision_attention_input_amd/csrc/pack.hip",
+                  "precision_attention_input_amd/csrc/ulp_device.h"]
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes the method must move (read + write), per step, by kernel.
+    N = B*S*H*D elements per tensor, e = 2 bytes, sigma = slots(L), W = scale width."""
+    import precision_attention_input_amd as ulp
+    e = 2
+    B, P, L, H, D = w.B, w.P, w.L, w.H, w.D
+    S = P * L
+    N = B * S * H * D
+    sigma = ulp.slots(L)
+    Wd = ulp.scale_widths(w.scale_sequence or S)[0]
+    spad = (S + 63) // 64 * 64
+    pack = 3 * e * N + 8 * B * H * sigma * P + P * e * B * H * D + 3 * N + 8 * B * H * sigma * P
+    unpack = 3 * N + 8 * B * H * Wd + 2 * N + B * D * H * spad + 8 * B * H * Wd
+    # fused statistics: read Q and K once, the mean per rank; write both amax tensors and
+    # both boundary min/max tensors
+    stats = 2 * e * N + P * e * B * H * D + 2 * 4 * B * H * sigma * P + 2 * 4 * P * B * H * 4 * D
+    return dict(pack=pack, unpack=unpack, stats=stats, N=N)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launch_bytes: int):
+    """HBM bytes per pack launch measured with rocprofv3 counters, if recorded for the
+    current kernel source; None otherwise."""
+    path = os.path.join(PROFILES, f"pack_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, reps: int):
+    """The CPU oracle's pack+unpack over the whole workload (every rank and destination),
+    repeated `reps` times, single-threaded."""
+    import torch
+    import oracle
+    from oracle import pipeline
+
+    P, L = w.P, w.L
+    qs, ks, vs = (pipeline.shards(d[n], P) for n in ("Q", "K", "V"))
+    # the amax the pack consumes (computed here, not timed: the metric is pack+unpack)
+    q_amax = [oracle.k_grouped_amax(qs[r], None, rank=r, world_size=P, used_sequence=w.used)
+              for r in range(P)]
+    k_amax = [oracle.k_grouped_amax(ks[r], d["mean"], rank=r, world_size=P,
+                                    used_sequence=w.used) for r in range(P)]
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        sends = [oracle.pack(qs[r], ks[r], vs[r], d["mean"], q_amax[r], k_amax[r], rank=r,
+                             world_size=P) for r in range(P)]
+        for p in range(P):
+            recv = torch.stack([sends[r][p] for r in range(P)])
+            oracle.unpack_for_sage(recv, batch_size=w.B, local_sequence=L, local_heads=w.h,
+                                   head_dim=w.D, world_size=P,
+                                   scale_sequence=w.scale_sequence)
+    dt = (time.perf_counter() - t0) / reps
+    return dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: the unaligned padded fp16 workload)")
+    ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (the whole Ulysses group is held "
+              f"by one device; world_size only shapes the byte layout); --gpus {args.gpus} "
+              f"is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import precision_attention_input_amd as ulp
+    from precision_attention_input_amd import workloads as W
+
+    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = W.generate(w)
+    nb = algorithmic_bytes(w)
+    set_bytes = 12 * nb["N"]      # stacked Q/K/V (6N) + all-to-all buffer (3N) + outputs (3N)
+    nsets = args.sets or max(2, min(8, -(-1024 * 2 ** 20 // set_bytes)))
+    P, L, B, H, D = w.P, w.L, w.B, w.H, w.D
+
+    sets = []
+    for i in range(nsets):
+        s = {n: W.stacked_shards(d[n], P).to(dev) for n in ("Q", "K", "V")}
+        s["mean"] = d["mean"].to(dev)
+        f = dict(dtype=torch.float32, device=dev)
+        sl = ulp.slots(L)
+        s["stats"] = (torch.empty(P, B, H, sl, **f), torch.empty(P, B, H, sl, **f),
+                      torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f))
+        s["group"] = ulp.group_buffer(B, L, H, D, P, dev)
+        s["out"] = ulp._alloc_unpack(dev, ulp.unpack_shapes(B, L, w.h, D, P, w.scale_sequence),
+                                     lead=(P,))
+        sets.append(s)
+
+    def step(s, ev=None):
+        if ev:
+            ev[0].record()
+        qa, ka, qm, km = ulp.group_stats(s["Q"], s["K"], s["mean"], world_size=P,
+                                         used_sequence=w.used, out=s["stats"])
+        if ev:
+            ev[1].record()
+        ulp.group_derive(qa, ka, qm, km, s["mean"], local_sequence=L, world_size=P)
+        if ev:
+            ev[2].record()
+        ulp.group_pack(s["Q"], s["K"], s["V"], s["mean"], qa, ka, world_size=P,
+                       group=s["group"])
+        if ev:
+            ev[3].record()
+        ulp.group_unpack(s["group"], batch_size=B, local_sequence=L, local_heads=w.h,
+                         head_dim=D, world_size=P, aligned=w.aligned,
+                         scale_sequence=w.scale_sequence, out=s["out"])
+        if ev:
+            ev[4].record()
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % nsets], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stats_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    derive_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    pack_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    unpack_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / K
+    ms_per_step = wall * 1e3 / K
+
+    pu_bytes = nb["pack"] + nb["unpack"]
+    value = pu_bytes / ((pack_ms + unpack_ms) * 1e-3) / 1e9
+    pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
+    traffic = load_traffic(w.name, nb["pack"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        dt = cpu_baseline(w, d, args.cpu_reps)
+        cpu = {"value": round(pu_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the whole workload: pack of all {P} ranks + unpack of all {P} "
+                         f"destinations, mean of {args.cpu_reps} repetitions "
+                         f"({dt:.3f} s each), single-threaded C oracle"}
+
+    line = {
+        "metric": "pack+unpack GB/s and % of HBM peak per config; amax-kernel GB/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "world_size": P, "local_sequence": L,
+                   "heads": H, "head_dim": D, "used_sequence": w.used,
+                   "scale_sequence": w.scale_sequence, "aligned": w.aligned,
+                   "buffer_sets": nsets},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "pack_unpack_bytes": pu_bytes,
+        "pack_ms": round(pack_ms, 5),
+        "unpack_ms": round(unpack_ms, 5),
+        "stats_ms": round(stats_ms, 5),
+        "derive_ms": round(derive_ms, 5),
+        "amax_gbps": round(nb["stats"] / (stats_ms * 1e-3) / 1e9, 2),
+        "step_gbps": round((pu_bytes + nb["stats"]) / (ms_per_step * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(pack_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": nb["pack"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * ulp.h -- C ABI of libulp: smooth-K low-precision Ulysses pack/unpack for SageAttention
+ * inputs, hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The method (FlashInfer pages flashinfer.comm._ulysses_lowp.k_grouped_amax,
+ * .derive_k_boundary_amax and .unpack_for_sage): in Ulysses sequence parallelism each of
+ * P = world_size ranks holds L = local_sequence consecutive rows of Q/K/V laid out
+ * [B, L, H, D]; an all-to-all regroups them so destination p holds the full sequence
+ * S = P*L for heads [p*h, (p+1)*h), h = H/P.  Instead of BF16/FP16 the exchange carries
+ * INT8 Q, INT8 mean-centered ("smooth") K, FP8 E4M3 V, and FP32 scales, one scale per
+ * 64-row group of the GLOBAL sequence.  A global group can straddle two shards; its amax
+ * is derived from raw-K min/max of every rank touching it, so one stats all-gather is
+ * enough.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte aligned.
+ *  - dtype is ULP_BF16 or ULP_FP16 and applies to every Q/K/V/k_mean operand of a call.
+ *  - head_dim D is 64 or 128; world_size P is 2, 4, 6 or 8 (6 accepted as on the pages);
+ *    B, L, H >= 1 and H % P == 0; 0 <= rank < P.
+ *  - used_sequence / scale_sequence: ULP_NONE (= None on the pages) or a value in [1, S].
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).  Calls are
+ *    asynchronous on that stream and never synchronize the host.
+ *  - The library allocates no device memory and keeps no state between calls except a
+ *    thread-local error message.  The caller owns every buffer.
+ *  - Outputs must not alias inputs (except the in-place amax of the derive call).
+ *  - Every output byte is written by every call, including unused slots and padding.
+ *  - Return value: ULP_OK, or an error code with NOTHING launched and nothing written;
+ *    ulp_last_error() then describes the problem.  ULP_ELAUNCH reports a HIP launch error.
+ *  - Zero-filling of rows >= used_sequence in Q, K and V is a caller contract
+ *    (k_grouped_amax, used_sequence parameter); it is not checked.
+ *
+ * Layouts (G = 64-row group size):
+ *  slots(L)      = L/64 if 64 divides L, else ceil(L/64) + 1: the most global groups an
+ *                  L-row shard can touch.  Slot j of rank r is global group
+ *                  g0(r) + j, g0(r) = floor(r*L/64); slots the rank does not touch hold
+ *                  the 1e-7 floor.
+ *  grouped amax  = float [B, H, slots(L)].
+ *  minmax        = float [B, H, 2, 2, D]: [.., e, s, d] with e = 0 the rank's first
+ *                  touched group, e = 1 its last; s = 0 min, s = 1 max.  Raw values over
+ *                  live rows (< used) only, -0 taken as +0; no live row gives
+ *                  (+inf, -inf).  The gathered form is [P, B, H, 2, 2, D] in rank order.
+ *  chunk         = the bytes source r sends destination p: sections q8 [B,L,h,D] int8,
+ *                  k8 [B,L,h,D] int8, v8 [B,L,h,D] E4M3 for heads p*h .. p*h+h-1, then
+ *                  q_scale [B,h,slots(L)] and k_scale [B,h,slots(L)] float; every section
+ *                  starts on a 256-byte boundary and gaps are zero.  Its size is
+ *                  ulp_chunk_bytes().
+ *  unpack output = q8, k8 int8 [B, S, h, D]; v8 E4M3 bytes [B, D, h, Spad] with
+ *                  Spad = ceil(S/64)*64 and columns [S, Spad) zero; q_scale, k_scale float
+ *                  [B, h, W] with W = ceil(n/64), n = scale_sequence or S.
+ */
+#ifndef ULP_H
+#define ULP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ULP_BF16 = 0, ULP_FP16 = 1 } ulp_dtype_t;
+
+enum {
+    ULP_OK = 0,
+    ULP_EINVAL = 1,        /* an argument is out of its domain, or a pointer is NULL */
+    ULP_EUNSUPPORTED = 2,  /* head_dim or world_size outside the supported set */
+    ULP_EALIGN = 3,        /* a pointer or stride is not suitably aligned */
+    ULP_ELAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+};
+
+#define ULP_NONE (-1)      /* None for used_sequence, scale_sequence and aligned */
+#define ULP_GROUP_ROWS 64  /* rows per scale group of the global sequence */
+
+/* slots(L, 64) as defined above; 0 when L < 1. */
+int64_t ulp_slots(int64_t local_sequence);
+
+/* Consumer scale widths for a live prefix of n rows (unpack_for_sage description: the
+ * Sage kernel derives its per-head scale stride from the rows it is given).  Writes
+ * ceil(n/64) to both outputs.  Returns ULP_EINVAL when n < 1 or a pointer is NULL. */
+int ulp_scale_widths(int64_t n, int64_t* q_width, int64_t* k_width);
+
+/* Bytes of one chunk (source -> destination) for batch B, local_sequence L, local_heads h,
+ * head_dim D; a multiple of 256.  0 when an argument is < 1. */
+int64_t ulp_chunk_bytes(int64_t B, int64_t L, int64_t h, int64_t D);
+
+/* Message for the last nonzero status returned on the calling thread ("" if none). */
+const char* ulp_last_error(void);
+
+/* k_grouped_amax (flashinfer.comm._ulysses_lowp.k_grouped_amax: description, Returns).
+ * Per touched global group, the partial amax over this rank's rows of the group and all D
+ * of |RN(fp32(x) - fp32(k_mean))|, an order-independent max, floored at 1e-7.  When
+ * used_sequence < S the one group mixing live rows and zero padding, (used-1)/64, is taken
+ * over its live rows only; with used_sequence ULP_NONE or S the result is bit-identical to
+ * the unfixed one.  Fully padded groups hold the (deterministic) value over their zero rows.
+ *   x       [B, L, H, D] dtype: this rank's shard (K, or Q with k_mean NULL).
+ *   k_mean  [B, H, D] dtype, the global K mean already rounded to dtype; NULL = raw values
+ *           (mean +0), which is how the Q amax is formed.
+ *   out     [B, H, slots(L)] float. */
+int ulp_k_grouped_amax(const void* x, const void* k_mean, int dtype, int64_t B, int64_t L,
+                       int64_t H, int64_t D, int rank, int world_size, int64_t used_sequence,
+                       float* out, void* stream);
+
+/* Raw boundary min/max of one rank's shard: the payload of the single stats all-gather
+ * that derive_k_boundary_amax consumes (its description and gathered_minmax parameter).
+ *   x    [B, L, H, D] dtype.
+ *   out  [B, H, 2, 2, D] float, layout above. */
+int ulp_boundary_minmax(const void* x, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+                        int rank, int world_size, int64_t used_sequence, float* out,
+                        void* stream);
+
+/* derive_k_boundary_amax (flashinfer.comm._ulysses_lowp.derive_k_boundary_amax:
+ * description).  For this rank's first and last touched groups g, overwrites slot
+ * g - g0(rank) with the max over every rank r touching g of
+ *   max(1e-7, max_d max(RN(maxK[r,g,d] - m[d]), RN(m[d] - minK[r,g,d]))),
+ * which equals the direct amax over all live rows of g, bit for bit.
+ *   grouped_amax     [B, H, slots(local_sequence)] float, updated in place.
+ *   gathered_minmax  [P, B, H, 2, 2, D] float in rank order.
+ *   k_mean           [B, H, D] dtype; NULL = mean +0 (the Q boundary merge). */
+int ulp_derive_k_boundary_amax(float* grouped_amax, const float* gathered_minmax,
+                               const void* k_mean, int dtype, int64_t B, int64_t H, int64_t D,
+                               int rank, int64_t local_sequence, int world_size, void* stream);
+
+/* Pack one rank's shard into P chunks (the pack kernel that k_grouped_amax's description
+ * says consumes the per-group scales; the chunks are the rows of the all-to-all buffer
+ * of unpack_for_sage's recv_u8 parameter).
+ * Per slot: scale = RN(amax / 127).  Per element of row l (slot of global row r*L + l):
+ *   q8 = clamp(rint(RN(fp32(q) / q_scale)), -127, 127)
+ *   k8 = clamp(rint(RN(RN(fp32(k) - fp32(k_mean)) / k_scale)), -127, 127)
+ *   v8 = E4M3FN(fp32(v)), round to nearest even, saturating to +-448.
+ *   q, k, v         [B, L, H, D] dtype.
+ *   k_mean          [B, H, D] dtype.
+ *   q_amax, k_amax  [B, H, slots(L)] float (after derive).
+ *   send            chunk for destination p at send + p * dest_stride_bytes; each chunk is
+ *                   ulp_chunk_bytes(B, L, H/P, D) bytes.  dest_stride_bytes must be a
+ *                   multiple of 256 and >= the chunk size. */
+int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
+             const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
+             int64_t D, int rank, int world_size, uint8_t* send, int64_t dest_stride_bytes,
+             void* stream);
+
+/* unpack_for_sage (flashinfer.comm._ulysses_lowp.unpack_for_sage: description, Returns).
+ * Turns the P received chunks into contiguous logical Q/K, transposed V with a zero global
+ * tail, and global-grid scales at the consumer width.  The scale of global group g comes
+ * from the source holding its first row, floor(64*g/L).  Outputs are identical for every
+ * value of aligned; aligned == 1 only asserts L % 128 == 0.
+ *   recv     [P, chunk_bytes] uint8, source-major.
+ *   aligned  ULP_NONE, 0 or 1.
+ *   q8, k8   [B, S, h, D] int8;  v8 [B, D, h, Spad] uint8;  q_scale, k_scale [B, h, W]. */
+int ulp_unpack_for_sage(const uint8_t* recv, int64_t B, int64_t L, int64_t h, int64_t D,
+                        int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
+                        int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale,
+                        void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Whole-group entry points.  On one GPU that holds the entire Ulysses group these run
+ * every rank (or every destination) of a step in a single launch each; results are
+ * bit-identical to calling the per-rank entry points above for every rank.
+ * Stacked shards are [P, B, L, H, D] (shard r = rows [r*L, (r+1)*L)).
+ * The all-to-all buffer is [P_dst, P_src, chunk_bytes]: what rank r sends destination p
+ * sits at group + (p*P + r) * chunk_bytes, and destination p's receive buffer is the
+ * contiguous [P, chunk_bytes] block at group + p*P*chunk_bytes.
+ * --------------------------------------------------------------------------------- */
+
+/* Both statistics of every rank in one pass over Q and K:
+ *   q_amax, k_amax    [P, B, H, slots(L)] float  (as ulp_k_grouped_amax per rank; Q raw)
+ *   q_minmax, k_minmax [P, B, H, 2, 2, D] float (as ulp_boundary_minmax per rank). */
+int ulp_group_stats(const void* q, const void* k, const void* k_mean, int dtype, int64_t B,
+                    int64_t L, int64_t H, int64_t D, int world_size, int64_t used_sequence,
+                    float* q_amax, float* k_amax, float* q_minmax, float* k_minmax,
+                    void* stream);
+
+/* ulp_derive_k_boundary_amax for every rank, for both Q (mean +0) and K. */
+int ulp_group_derive(float* q_amax, float* k_amax, const float* q_minmax,
+                     const float* k_minmax, const void* k_mean, int dtype, int64_t B,
+                     int64_t H, int64_t D, int64_t local_sequence, int world_size,
+                     void* stream);
+
+/* ulp_pack for every rank into the all-to-all buffer `group` (layout above). */
+int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
+                   const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
+                   int64_t D, int world_size, uint8_t* group, void* stream);
+
+/* ulp_unpack_for_sage for every destination; outputs are stacked over destinations:
+ * q8, k8 [P, B, S, h, D]; v8 [P, B, D, h, Spad]; q_scale, k_scale [P, B, h, W]. */
+int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int64_t D,
+                     int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
+                     int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULP_H */

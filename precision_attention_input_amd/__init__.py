@@ -1,0 +1,277 @@
+"""Smooth-K low-precision Ulysses pack/unpack for SageAttention inputs on MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libulp.so`` (declared in ``include/ulp.h``):
+argument marshalling only.  Every step runs in the library's HIP kernels; torch provides
+device memory and the current stream.  There is no fallback: when the library is missing,
+every call raises.
+
+Per-rank functions mirror the FlashInfer pages ``flashinfer.comm._ulysses_lowp``:
+``k_grouped_amax``, ``derive_k_boundary_amax`` and ``unpack_for_sage`` (the pages'
+``enable_pdl`` has no counterpart: launches are ordered on the current stream), plus
+``boundary_minmax`` (the stats all-gather payload) and ``pack``.  The ``group_*`` functions
+run a whole Ulysses group held by one GPU with one launch per step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
+    "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
+    "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer",
+    "unpack_shapes",
+]
+
+ULP_NONE = -1
+GROUP_ROWS = 64
+_OK, _EINVAL, _EUNSUPPORTED, _EALIGN, _ELAUNCH = 0, 1, 2, 3, 4
+_DTYPES = {torch.bfloat16: 0, torch.float16: 1}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libulp.so")
+_lib = None
+
+
+class UlpError(RuntimeError):
+    """A kernel launch failed (ULP_ELAUNCH)."""
+
+
+def lib():
+    """The loaded libulp.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it first (python -c "
+                "'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        sig = {
+            "ulp_slots": ([i64], i64),
+            "ulp_scale_widths": ([i64, vp, vp], i32),
+            "ulp_chunk_bytes": ([i64, i64, i64, i64], i64),
+            "ulp_last_error": ([], ctypes.c_char_p),
+            "ulp_k_grouped_amax": ([vp, vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
+            "ulp_boundary_minmax": ([vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
+            "ulp_derive_k_boundary_amax": ([vp, vp, vp, i32, i64, i64, i64, i32, i64, i32, vp],
+                                           i32),
+            "ulp_pack": ([vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64, vp],
+                         i32),
+            "ulp_unpack_for_sage": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp,
+                                     vp], i32),
+            "ulp_group_stats": ([vp, vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, vp, vp, vp,
+                                 vp], i32),
+            "ulp_group_derive": ([vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp], i32),
+            "ulp_group_pack": ([vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, vp, vp],
+                               i32),
+            "ulp_group_unpack": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp],
+                                 i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc == _OK:
+        return
+    msg = lib().ulp_last_error().decode()
+    if rc == _ELAUNCH:
+        raise UlpError(msg)
+    raise ValueError(msg)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"expected bfloat16 or float16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _none(v):
+    return ULP_NONE if v is None else int(v)
+
+
+def slots(local_sequence: int) -> int:
+    """slots(L, 64): the most 64-row global groups an L-row shard can touch."""
+    return int(lib().ulp_slots(local_sequence))
+
+
+def chunk_bytes(batch_size: int, local_sequence: int, local_heads: int, head_dim: int) -> int:
+    return int(lib().ulp_chunk_bytes(batch_size, local_sequence, local_heads, head_dim))
+
+
+def scale_widths(n: int) -> tuple[int, int]:
+    """(q_width, k_width) of the scale tensors for a live prefix of n rows."""
+    q, k = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ulp_scale_widths(n, ctypes.byref(q), ctypes.byref(k)))
+    return q.value, k.value
+
+
+def unpack_shapes(batch_size, local_sequence, local_heads, head_dim, world_size,
+                  scale_sequence=None):
+    S = world_size * local_sequence
+    spad = (S + GROUP_ROWS - 1) // GROUP_ROWS * GROUP_ROWS
+    W = scale_widths(scale_sequence or S)[0]
+    B, h, D = batch_size, local_heads, head_dim
+    return (B, S, h, D), (B, D, h, spad), (B, h, W)
+
+
+# ------------------------------------------------------------------------- per rank
+
+def k_grouped_amax(k, k_mean_global, *, rank, world_size, used_sequence=None, out=None):
+    """[B, H, slots(L)] fp32 partial amax of |K - k_mean_global| (k_mean_global None: raw
+    values, the Q amax).  flashinfer.comm._ulysses_lowp.k_grouped_amax."""
+    _dev(k, k_mean_global, out)
+    B, L, H, D = k.shape
+    if out is None:
+        out = torch.empty(B, H, slots(L), dtype=torch.float32, device=k.device)
+    _check(lib().ulp_k_grouped_amax(_p(k), _p(k_mean_global), _dt(k), B, L, H, D, rank,
+                                    world_size, _none(used_sequence), _p(out), _stream(k)))
+    return out
+
+
+def boundary_minmax(x, *, rank, world_size, used_sequence=None, out=None):
+    """[B, H, 2, 2, D] fp32 raw min/max of the live rows of the rank's first/last group."""
+    _dev(x, out)
+    B, L, H, D = x.shape
+    if out is None:
+        out = torch.empty(B, H, 2, 2, D, dtype=torch.float32, device=x.device)
+    _check(lib().ulp_boundary_minmax(_p(x), _dt(x), B, L, H, D, rank, world_size,
+                                     _none(used_sequence), _p(out), _stream(x)))
+    return out
+
+
+def derive_k_boundary_amax(grouped_amax, gathered_minmax, k_mean_global, *, rank,
+                           local_sequence, world_size):
+    """Overwrites this rank's boundary slots in place and returns ``grouped_amax``.
+    flashinfer.comm._ulysses_lowp.derive_k_boundary_amax.  k_mean_global None: mean +0."""
+    _dev(grouped_amax, gathered_minmax, k_mean_global)
+    P, B, H, _, _, D = gathered_minmax.shape
+    dt = _dt(k_mean_global) if k_mean_global is not None else 0
+    _check(lib().ulp_derive_k_boundary_amax(_p(grouped_amax), _p(gathered_minmax),
+                                            _p(k_mean_global), dt, B, H, D, rank,
+                                            local_sequence, world_size,
+                                            _stream(grouped_amax)))
+    return grouped_amax
+
+
+def pack(q, k, v, k_mean_global, q_amax, k_amax, *, rank, world_size, send=None,
+         dest_stride=None):
+    """Quantize one rank's shard; returns the send buffer [world_size, chunk_bytes] uint8
+    (or writes chunk p at ``send`` + p * dest_stride bytes when ``send`` is given)."""
+    _dev(q, k, v, k_mean_global, q_amax, k_amax)
+    B, L, H, D = q.shape
+    cb = chunk_bytes(B, L, H // world_size, D)
+    if send is None:
+        send = torch.empty(world_size, cb, dtype=torch.uint8, device=q.device)
+        dest_stride = cb
+    _check(lib().ulp_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
+                          _p(k_amax), B, L, H, D, rank, world_size, _p(send),
+                          dest_stride or cb, _stream(q)))
+    return send
+
+
+def _alloc_unpack(device, shapes, lead=()):
+    qk, vs, sc = shapes
+    return (torch.empty(*lead, *qk, dtype=torch.int8, device=device),
+            torch.empty(*lead, *qk, dtype=torch.int8, device=device),
+            torch.empty(*lead, *vs, dtype=torch.float8_e4m3fn, device=device),
+            torch.empty(*lead, *sc, dtype=torch.float32, device=device),
+            torch.empty(*lead, *sc, dtype=torch.float32, device=device))
+
+
+def unpack_for_sage(recv_u8, *, batch_size, local_sequence, local_heads, head_dim, world_size,
+                    aligned=None, scale_sequence=None, out=None):
+    """(q8, k8, v8, q_scale, k_scale): INT8 [B,S,h,D] x2, FP8 E4M3 [B,D,h,ceil(S/64)*64],
+    FP32 [B,h,W] x2.  flashinfer.comm._ulysses_lowp.unpack_for_sage."""
+    if out is None:
+        out = _alloc_unpack(recv_u8.device, unpack_shapes(batch_size, local_sequence,
+                                                          local_heads, head_dim, world_size,
+                                                          scale_sequence))
+    _dev(recv_u8, *out)
+    q8, k8, v8, qs, ks = out
+    _check(lib().ulp_unpack_for_sage(_p(recv_u8), batch_size, local_sequence, local_heads,
+                                     head_dim, world_size, _none(aligned),
+                                     _none(scale_sequence), _p(q8), _p(k8), _p(v8), _p(qs),
+                                     _p(ks), _stream(recv_u8)))
+    return tuple(out)
+
+
+# ------------------------------------------------------------------------- whole group
+
+def group_stats(q, k, k_mean_global, *, world_size, used_sequence=None, out=None):
+    """Stacked shards [P,B,L,H,D] -> (q_amax, k_amax [P,B,H,slots], q_minmax, k_minmax
+    [P,B,H,2,2,D]) in one launch."""
+    P, B, L, H, D = q.shape
+    if out is None:
+        f = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty(P, B, H, slots(L), **f), torch.empty(P, B, H, slots(L), **f),
+               torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f))
+    _dev(q, k, k_mean_global, *out)
+    qa, ka, qm, km = out
+    _check(lib().ulp_group_stats(_p(q), _p(k), _p(k_mean_global), _dt(q), B, L, H, D,
+                                 world_size, _none(used_sequence), _p(qa), _p(ka), _p(qm),
+                                 _p(km), _stream(q)))
+    return tuple(out)
+
+
+def group_derive(q_amax, k_amax, q_minmax, k_minmax, k_mean_global, *, local_sequence,
+                 world_size):
+    """Boundary derive of every rank for Q and K, in place; returns (q_amax, k_amax)."""
+    _dev(q_amax, k_amax, q_minmax, k_minmax, k_mean_global)
+    P, B, H, _, _, D = k_minmax.shape
+    _check(lib().ulp_group_derive(_p(q_amax), _p(k_amax), _p(q_minmax), _p(k_minmax),
+                                  _p(k_mean_global), _dt(k_mean_global), B, H, D,
+                                  local_sequence, world_size, _stream(q_amax)))
+    return q_amax, k_amax
+
+
+def group_buffer(batch_size, local_sequence, heads, head_dim, world_size, device):
+    """An all-to-all buffer [P_dst, P_src, chunk_bytes] uint8."""
+    cb = chunk_bytes(batch_size, local_sequence, heads // world_size, head_dim)
+    return torch.empty(world_size, world_size, cb, dtype=torch.uint8, device=device)
+
+
+def group_pack(q, k, v, k_mean_global, q_amax, k_amax, *, world_size, group=None):
+    """Every rank's pack into the all-to-all buffer [P_dst, P_src, chunk_bytes]."""
+    P, B, L, H, D = q.shape
+    if group is None:
+        group = group_buffer(B, L, H, D, world_size, q.device)
+    _dev(q, k, v, k_mean_global, q_amax, k_amax, group)
+    _check(lib().ulp_group_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
+                                _p(k_amax), B, L, H, D, world_size, _p(group), _stream(q)))
+    return group
+
+
+def group_unpack(group, *, batch_size, local_sequence, local_heads, head_dim, world_size,
+                 aligned=None, scale_sequence=None, out=None):
+    """Every destination's unpack; outputs stacked over destinations."""
+    if out is None:
+        out = _alloc_unpack(group.device, unpack_shapes(batch_size, local_sequence,
+                                                        local_heads, head_dim, world_size,
+                                                        scale_sequence), lead=(world_size,))
+    _dev(group, *out)
+    q8, k8, v8, qs, ks = out
+    _check(lib().ulp_group_unpack(_p(group), batch_size, local_sequence, local_heads,
+                                  head_dim, world_size, _none(aligned), _none(scale_sequence),
+                                  _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _stream(group)))
+    return tuple(out)

@@ -1,0 +1,346 @@
+// api.hip -- the C ABI of libulp: argument validation and kernel launches.
+//
+// Every entry point validates all of its arguments on the host before launching anything;
+// an invalid call returns an error code, launches nothing and leaves a message for
+// ulp_last_error().  No entry point allocates device memory or synchronizes the host.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ulp.h"
+#include "ulp_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ULP_ELAUNCH, "%s: kernel launch failed: %s", what,
+                                     hipGetErrorString(e));
+    return ULP_OK;
+}
+
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+// Shared domain checks (pages: world_size one of 2/4/6/8, head_dim 64 or 128, H divisible
+// by world_size).  rank < 0 skips the rank check.
+int check_shape(const char* fn, int dtype, int64_t B, int64_t L, int64_t H, int64_t D, int P,
+                int rank, bool check_rank) {
+    if (dtype != ULP_BF16 && dtype != ULP_FP16)
+        return fail(ULP_EINVAL, "%s: dtype must be ULP_BF16 (0) or ULP_FP16 (1), got %d", fn,
+                    dtype);
+    if (D != 64 && D != 128)
+        return fail(ULP_EUNSUPPORTED, "%s: head_dim must be 64 or 128, got %lld", fn,
+                    (long long)D);
+    if (P != 2 && P != 4 && P != 6 && P != 8)
+        return fail(ULP_EUNSUPPORTED, "%s: world_size must be 2, 4, 6 or 8, got %d", fn, P);
+    if (check_rank && (rank < 0 || rank >= P))
+        return fail(ULP_EINVAL, "%s: rank %d outside [0, %d)", fn, rank, P);
+    if (B < 1 || L < 1 || H < 1)
+        return fail(ULP_EINVAL, "%s: batch, local_sequence and heads must be >= 1 "
+                                "(got B=%lld L=%lld H=%lld)", fn, (long long)B, (long long)L,
+                    (long long)H);
+    if (H % P != 0)
+        return fail(ULP_EINVAL, "%s: heads %lld not divisible by world_size %d", fn,
+                    (long long)H, P);
+    // Keep every element offset far from int64 overflow and every grid within HIP limits.
+    const int64_t lim = (int64_t)1 << 40;
+    if (B > lim / L || B * L > lim / H || B * L * H > lim / (D * P))
+        return fail(ULP_EINVAL, "%s: problem too large", fn);
+    const int64_t slots = ulp::slots_of(L);
+    if (B * slots * ((H + 1) / 2) >= kMaxGrid)
+        return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
+    return ULP_OK;
+}
+
+int check_seq(const char* fn, const char* name, int64_t v, int64_t S) {
+    if (v == ULP_NONE || (v >= 1 && v <= S)) return ULP_OK;
+    return fail(ULP_EINVAL, "%s: %s must be ULP_NONE or in [1, %lld], got %lld", fn, name,
+                (long long)S, (long long)v);
+}
+
+int check_ptr(const char* fn, const char* name, const void* p) {
+    if (p == nullptr) return fail(ULP_EINVAL, "%s: %s is NULL", fn, name);
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+        return fail(ULP_EALIGN, "%s: %s is not 16-byte aligned", fn, name);
+    return ULP_OK;
+}
+
+int check_aligned_flag(const char* fn, int aligned, int64_t L) {
+    if (aligned != ULP_NONE && aligned != 0 && aligned != 1)
+        return fail(ULP_EINVAL, "%s: aligned must be ULP_NONE, 0 or 1, got %d", fn, aligned);
+    if (aligned == 1 && L % 128 != 0)
+        return fail(ULP_EINVAL, "%s: aligned=True requires local_sequence %% 128 == 0 "
+                                "(local_sequence=%lld)", fn, (long long)L);
+    return ULP_OK;
+}
+
+#define TRY(expr)                  \
+    do {                           \
+        int rc_ = (expr);          \
+        if (rc_ != ULP_OK) return rc_; \
+    } while (0)
+
+int64_t used_or_s(int64_t used, int64_t S) { return used == ULP_NONE ? S : used; }
+int64_t width_of(int64_t n) { return (n + ULP_GROUP_ROWS - 1) / ULP_GROUP_ROWS; }
+
+}  // namespace
+
+namespace ulp {
+int64_t unpack_blocks(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W);
+}
+
+extern "C" {
+
+int64_t ulp_slots(int64_t local_sequence) {
+    return local_sequence < 1 ? 0 : ulp::slots_of(local_sequence);
+}
+
+int ulp_scale_widths(int64_t n, int64_t* q_width, int64_t* k_width) {
+    if (n < 1) return fail(ULP_EINVAL, "ulp_scale_widths: n must be >= 1, got %lld", (long long)n);
+    if (!q_width || !k_width) return fail(ULP_EINVAL, "ulp_scale_widths: NULL output");
+    *q_width = width_of(n);
+    *k_width = width_of(n);
+    return ULP_OK;
+}
+
+int64_t ulp_chunk_bytes(int64_t B, int64_t L, int64_t h, int64_t D) {
+    if (B < 1 || L < 1 || h < 1 || D < 1) return 0;
+    return ulp::chunk_bytes_of(B, L, h, D);
+}
+
+const char* ulp_last_error(void) { return g_last_error.c_str(); }
+
+int ulp_k_grouped_amax(const void* x, const void* k_mean, int dtype, int64_t B, int64_t L,
+                       int64_t H, int64_t D, int rank, int world_size, int64_t used_sequence,
+                       float* out, void* stream) {
+    const char* fn = "ulp_k_grouped_amax";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, rank, true));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "x", x));
+    if (k_mean) TRY(check_ptr(fn, "k_mean", k_mean));
+    TRY(check_ptr(fn, "out", out));
+    ulp::StatsLaunch a{};
+    a.x[0] = static_cast<const uint16_t*>(x);
+    a.mean[0] = static_cast<const uint16_t*>(k_mean);
+    a.amax[0] = out;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.used = used_or_s(used_sequence, world_size * L);
+    a.rank0 = rank; a.nranks = 1; a.dtype = dtype;
+    return launched(ulp::launch_stats(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_boundary_minmax(const void* x, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+                        int rank, int world_size, int64_t used_sequence, float* out,
+                        void* stream) {
+    const char* fn = "ulp_boundary_minmax";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, rank, true));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "x", x));
+    TRY(check_ptr(fn, "out", out));
+    ulp::StatsLaunch a{};
+    a.x[0] = static_cast<const uint16_t*>(x);
+    a.minmax[0] = out;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.used = used_or_s(used_sequence, world_size * L);
+    a.rank0 = rank; a.nranks = 1; a.dtype = dtype;
+    return launched(ulp::launch_stats(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_derive_k_boundary_amax(float* grouped_amax, const float* gathered_minmax,
+                               const void* k_mean, int dtype, int64_t B, int64_t H, int64_t D,
+                               int rank, int64_t local_sequence, int world_size, void* stream) {
+    const char* fn = "ulp_derive_k_boundary_amax";
+    TRY(check_shape(fn, dtype, B, local_sequence, H, D, world_size, rank, true));
+    TRY(check_ptr(fn, "grouped_amax", grouped_amax));
+    TRY(check_ptr(fn, "gathered_minmax", gathered_minmax));
+    if (k_mean) TRY(check_ptr(fn, "k_mean", k_mean));
+    ulp::DeriveLaunch a{};
+    a.amax[0] = grouped_amax;
+    a.minmax[0] = gathered_minmax;
+    a.mean[0] = static_cast<const uint16_t*>(k_mean);
+    a.B = B; a.H = H; a.D = D; a.L = local_sequence; a.P = world_size;
+    a.rank0 = rank; a.nranks = 1; a.dtype = dtype;
+    return launched(ulp::launch_derive(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
+             const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
+             int64_t D, int rank, int world_size, uint8_t* send, int64_t dest_stride_bytes,
+             void* stream) {
+    const char* fn = "ulp_pack";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, rank, true));
+    TRY(check_ptr(fn, "q", q));
+    TRY(check_ptr(fn, "k", k));
+    TRY(check_ptr(fn, "v", v));
+    TRY(check_ptr(fn, "k_mean", k_mean));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    TRY(check_ptr(fn, "send", send));
+    const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
+    if (dest_stride_bytes % 256 != 0)
+        return fail(ULP_EALIGN, "%s: dest_stride_bytes %lld is not a multiple of 256", fn,
+                    (long long)dest_stride_bytes);
+    if (dest_stride_bytes < cb)
+        return fail(ULP_EINVAL, "%s: dest_stride_bytes %lld is smaller than the chunk (%lld)",
+                    fn, (long long)dest_stride_bytes, (long long)cb);
+    ulp::PackLaunch a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.mean = static_cast<const uint16_t*>(k_mean);
+    a.q_amax = q_amax;
+    a.k_amax = k_amax;
+    a.send = send;
+    a.dest_stride = dest_stride_bytes;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.rank0 = rank; a.nranks = 1; a.dtype = dtype;
+    return launched(ulp::launch_pack(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+static int unpack_common(const char* fn, const uint8_t* recv, int64_t B, int64_t L, int64_t h,
+                         int64_t D, int world_size, int aligned, int64_t scale_sequence,
+                         int8_t* q8, int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale,
+                         int ndests, void* stream) {
+    if (h < 1) return fail(ULP_EINVAL, "%s: local_heads must be >= 1, got %lld", fn, (long long)h);
+    TRY(check_shape(fn, ULP_BF16, B, L, h * world_size, D, world_size, 0, false));
+    TRY(check_aligned_flag(fn, aligned, L));
+    const int64_t S = world_size * L;
+    TRY(check_seq(fn, "scale_sequence", scale_sequence, S));
+    TRY(check_ptr(fn, "recv", recv));
+    TRY(check_ptr(fn, "q8", q8));
+    TRY(check_ptr(fn, "k8", k8));
+    TRY(check_ptr(fn, "v8", v8));
+    TRY(check_ptr(fn, "q_scale", q_scale));
+    TRY(check_ptr(fn, "k_scale", k_scale));
+    const int64_t W = width_of(scale_sequence == ULP_NONE ? S : scale_sequence);
+    if (ulp::unpack_blocks(B, L, h, D, world_size, W) >= kMaxGrid)
+        return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
+    const int64_t spad = (S + ULP_GROUP_ROWS - 1) / ULP_GROUP_ROWS * ULP_GROUP_ROWS;
+    const int64_t cb = ulp::chunk_bytes_of(B, L, h, D);
+    ulp::UnpackLaunch a{};
+    a.recv = recv;
+    a.recv_dest_stride = (int64_t)world_size * cb;
+    a.q8 = q8;
+    a.k8 = k8;
+    a.v8 = v8;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.qk_dest_stride = B * S * h * D;
+    a.v_dest_stride = B * D * h * spad;
+    a.scale_dest_stride = B * h * W;
+    a.B = B; a.L = L; a.h = h; a.D = D; a.P = world_size; a.W = W;
+    a.ndests = ndests;
+    return launched(ulp::launch_unpack(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_unpack_for_sage(const uint8_t* recv, int64_t B, int64_t L, int64_t h, int64_t D,
+                        int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
+                        int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, void* stream) {
+    return unpack_common("ulp_unpack_for_sage", recv, B, L, h, D, world_size, aligned,
+                         scale_sequence, q8, k8, v8, q_scale, k_scale, 1, stream);
+}
+
+int ulp_group_stats(const void* q, const void* k, const void* k_mean, int dtype, int64_t B,
+                    int64_t L, int64_t H, int64_t D, int world_size, int64_t used_sequence,
+                    float* q_amax, float* k_amax, float* q_minmax, float* k_minmax,
+                    void* stream) {
+    const char* fn = "ulp_group_stats";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "q", q));
+    TRY(check_ptr(fn, "k", k));
+    TRY(check_ptr(fn, "k_mean", k_mean));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    TRY(check_ptr(fn, "q_minmax", q_minmax));
+    TRY(check_ptr(fn, "k_minmax", k_minmax));
+    ulp::StatsLaunch a{};
+    a.x[0] = static_cast<const uint16_t*>(q);
+    a.x[1] = static_cast<const uint16_t*>(k);
+    a.mean[1] = static_cast<const uint16_t*>(k_mean);
+    a.amax[0] = q_amax;
+    a.amax[1] = k_amax;
+    a.minmax[0] = q_minmax;
+    a.minmax[1] = k_minmax;
+    a.x_rank_stride = B * L * H * D;
+    a.amax_rank_stride = B * H * ulp::slots_of(L);
+    a.minmax_rank_stride = B * H * 4 * D;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.used = used_or_s(used_sequence, world_size * L);
+    a.rank0 = 0; a.nranks = world_size; a.dtype = dtype;
+    return launched(ulp::launch_stats(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_group_derive(float* q_amax, float* k_amax, const float* q_minmax,
+                     const float* k_minmax, const void* k_mean, int dtype, int64_t B,
+                     int64_t H, int64_t D, int64_t local_sequence, int world_size,
+                     void* stream) {
+    const char* fn = "ulp_group_derive";
+    TRY(check_shape(fn, dtype, B, local_sequence, H, D, world_size, 0, false));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    TRY(check_ptr(fn, "q_minmax", q_minmax));
+    TRY(check_ptr(fn, "k_minmax", k_minmax));
+    TRY(check_ptr(fn, "k_mean", k_mean));
+    ulp::DeriveLaunch a{};
+    a.amax[0] = q_amax;
+    a.amax[1] = k_amax;
+    a.minmax[0] = q_minmax;
+    a.minmax[1] = k_minmax;
+    a.mean[1] = static_cast<const uint16_t*>(k_mean);
+    a.amax_rank_stride = B * H * ulp::slots_of(local_sequence);
+    a.B = B; a.H = H; a.D = D; a.L = local_sequence; a.P = world_size;
+    a.rank0 = 0; a.nranks = world_size; a.dtype = dtype;
+    return launched(ulp::launch_derive(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
+                   const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
+                   int64_t D, int world_size, uint8_t* group, void* stream) {
+    const char* fn = "ulp_group_pack";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
+    TRY(check_ptr(fn, "q", q));
+    TRY(check_ptr(fn, "k", k));
+    TRY(check_ptr(fn, "v", v));
+    TRY(check_ptr(fn, "k_mean", k_mean));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    TRY(check_ptr(fn, "group", group));
+    const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
+    ulp::PackLaunch a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.mean = static_cast<const uint16_t*>(k_mean);
+    a.q_amax = q_amax;
+    a.k_amax = k_amax;
+    a.send = group;
+    a.dest_stride = (int64_t)world_size * cb;
+    a.x_rank_stride = B * L * H * D;
+    a.amax_rank_stride = B * H * ulp::slots_of(L);
+    a.send_rank_stride = cb;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.rank0 = 0; a.nranks = world_size; a.dtype = dtype;
+    return launched(ulp::launch_pack(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int64_t D,
+                     int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
+                     int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, void* stream) {
+    return unpack_common("ulp_group_unpack", group, B, L, h, D, world_size, aligned,
+                         scale_sequence, q8, k8, v8, q_scale, k_scale, world_size, stream);
+}
+
+}  // extern "C"

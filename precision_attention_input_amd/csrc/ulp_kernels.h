@@ -1,0 +1,71 @@
+// ulp_kernels.h -- host-side launch descriptors of the libulp kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ulp {
+
+// Grouped amax and/or boundary min/max over one or more ranks' shards, for up to two
+// tensors (index 0 and 1 of the arrays; a tensor with x == nullptr is skipped).
+struct StatsLaunch {
+    const uint16_t* x[2];     // shard of rank rank0 [B, L, H, D]
+    const uint16_t* mean[2];  // [B, H, D] or nullptr (raw values)
+    float* amax[2];           // [B, H, slots] or nullptr (not wanted)
+    float* minmax[2];         // [B, H, 2, 2, D] or nullptr (not wanted)
+    int64_t x_rank_stride;    // elements between consecutive ranks' shards
+    int64_t amax_rank_stride;
+    int64_t minmax_rank_stride;
+    int64_t B, L, H, D, P, used;  // used = S when None
+    int rank0, nranks, dtype;
+};
+
+struct DeriveLaunch {
+    float* amax[2];             // [B, H, slots] of rank rank0, updated in place
+    const float* minmax[2];     // gathered [P, B, H, 2, 2, D]
+    const uint16_t* mean[2];    // [B, H, D] or nullptr (+0)
+    int64_t amax_rank_stride;
+    int64_t B, H, D, L, P;
+    int rank0, nranks, dtype;
+};
+
+struct PackLaunch {
+    const uint16_t *q, *k, *v, *mean;   // shards of rank rank0 [B, L, H, D]; mean [B, H, D]
+    const float *q_amax, *k_amax;       // [B, H, slots] of rank rank0
+    uint8_t* send;                      // chunk (rank0 -> p) at send + p * dest_stride
+    int64_t dest_stride;
+    int64_t x_rank_stride, amax_rank_stride, send_rank_stride;
+    int64_t B, L, H, D, P;
+    int rank0, nranks, dtype;
+};
+
+struct UnpackLaunch {
+    const uint8_t* recv;           // [P, chunk_bytes] of destination 0 of this launch
+    int64_t recv_dest_stride;      // bytes between consecutive destinations' recv blocks
+    int8_t *q8, *k8;
+    uint8_t* v8;
+    float *q_scale, *k_scale;
+    int64_t qk_dest_stride, v_dest_stride, scale_dest_stride;   // elements per destination
+    int64_t B, L, h, D, P, W;
+    int ndests;
+};
+
+hipError_t launch_stats(const StatsLaunch& a, hipStream_t stream);
+hipError_t launch_derive(const DeriveLaunch& a, hipStream_t stream);
+hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
+hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream);
+
+// Geometry shared by host and kernels.
+inline int64_t slots_of(int64_t L) { return L % 64 == 0 ? L / 64 : (L + 63) / 64 + 1; }
+inline int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+inline int64_t chunk_section(int64_t B, int64_t L, int64_t h, int64_t D) {
+    return align256(B * L * h * D);
+}
+inline int64_t chunk_scale_section(int64_t B, int64_t L, int64_t h) {
+    return align256(4 * B * h * slots_of(L));
+}
+inline int64_t chunk_bytes_of(int64_t B, int64_t L, int64_t h, int64_t D) {
+    return 3 * chunk_section(B, L, h, D) + 2 * chunk_scale_section(B, L, h);
+}
+
+}  // namespace ulp

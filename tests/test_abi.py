@@ -1,0 +1,136 @@
+"""The C ABI of libulp.so without a GPU: every symbol declared in include/ulp.h is exported,
+the geometry helpers agree with the oracle, and every validation error is reported with
+its code before anything is launched (CPU only: no call here reaches a kernel)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import precision_attention_input_amd as ulp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulp.h")
+
+OK, EINVAL, EUNSUPPORTED, EALIGN = 0, 1, 2, 3
+NONE = -1
+A = 0x10000          # a fake, 16-byte aligned address: validation rejects before any use
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ulp.LIB_PATH):
+        from precision_attention_input_amd import _build
+        _build.build()
+    return ulp.lib()
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ulp_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared()
+    assert "ulp_pack" in names and "ulp_unpack_for_sage" in names and len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_geometry_helpers_match_oracle(L, olib):
+    for Lseq in [1, 2, 31, 63, 64, 65, 96, 100, 127, 128, 129, 200, 1000, 2048, 4096, 9360]:
+        assert ulp.slots(Lseq) == oracle.slots(Lseq)
+        for (B, h, D) in [(1, 1, 64), (2, 4, 128), (4, 12, 64), (1, 5, 128)]:
+            assert ulp.chunk_bytes(B, Lseq, h, D) == oracle.chunk_bytes(B, Lseq, h, D)
+            assert ulp.chunk_bytes(B, Lseq, h, D) % 256 == 0
+    assert ulp.scale_widths(3700) == (58, 58)
+    assert ulp.scale_widths(1) == (1, 1)
+    assert ulp.scale_widths(64) == (1, 1) and ulp.scale_widths(65) == (2, 2)
+    assert L.ulp_slots(0) == 0 and L.ulp_chunk_bytes(0, 1, 1, 64) == 0
+
+
+def test_scale_widths_rejects_empty_prefix(L):
+    q, k = ctypes.c_int64(), ctypes.c_int64()
+    assert L.ulp_scale_widths(0, ctypes.byref(q), ctypes.byref(k)) == EINVAL
+    assert b"n must be" in L.ulp_last_error()
+
+
+def amax_call(L, dtype=0, B=1, Lq=128, H=4, D=64, rank=0, P=2, used=NONE, x=A, mean=A, out=A):
+    return L.ulp_k_grouped_amax(x, mean, dtype, B, Lq, H, D, rank, P, used, out, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dtype=2), EINVAL, b"dtype"),
+    (dict(D=96), EUNSUPPORTED, b"head_dim"),
+    (dict(P=3, H=6), EUNSUPPORTED, b"world_size"),
+    (dict(P=16, H=16), EUNSUPPORTED, b"world_size"),
+    (dict(rank=2), EINVAL, b"rank"),
+    (dict(rank=-1), EINVAL, b"rank"),
+    (dict(H=3), EINVAL, b"divisible"),
+    (dict(B=0), EINVAL, b">= 1"),
+    (dict(Lq=0), EINVAL, b">= 1"),
+    (dict(used=0), EINVAL, b"used_sequence"),
+    (dict(used=257), EINVAL, b"used_sequence"),
+    (dict(used=-5), EINVAL, b"used_sequence"),
+    (dict(x=0), EINVAL, b"NULL"),
+    (dict(out=0), EINVAL, b"NULL"),
+    (dict(x=A + 2), EALIGN, b"aligned"),
+    (dict(mean=A + 8), EALIGN, b"aligned"),
+    (dict(B=1 << 30, Lq=1 << 20), EINVAL, b"too large"),
+])
+def test_amax_validation(L, kw, code, msg):
+    assert amax_call(L, **kw) == code
+    assert msg in L.ulp_last_error()
+
+
+def test_minmax_and_derive_validation(L):
+    assert L.ulp_boundary_minmax(A, 0, 1, 128, 4, 128, 5, 4, NONE, A, None) == EINVAL
+    assert L.ulp_boundary_minmax(A, 1, 1, 128, 4, 128, 0, 4, 513, A, None) == EINVAL
+    assert L.ulp_boundary_minmax(A, 1, 1, 128, 4, 32, 0, 4, NONE, A, None) == EUNSUPPORTED
+    assert L.ulp_derive_k_boundary_amax(0, A, A, 0, 1, 4, 64, 0, 128, 2, None) == EINVAL
+    assert L.ulp_derive_k_boundary_amax(A, A + 4, A, 0, 1, 4, 64, 0, 128, 2, None) == EALIGN
+    assert L.ulp_derive_k_boundary_amax(A, A, A, 0, 1, 5, 64, 0, 128, 2, None) == EINVAL
+
+
+def test_pack_validation(L):
+    cb = ulp.chunk_bytes(1, 128, 2, 64)
+    args = [A, A, A, A, 0, A, A, 1, 128, 4, 64, 0, 2, A]
+    assert L.ulp_pack(*args, cb + 16, None) == EALIGN
+    assert b"multiple of 256" in L.ulp_last_error()
+    assert L.ulp_pack(*args, cb - 256, None) == EINVAL
+    assert b"smaller than the chunk" in L.ulp_last_error()
+    bad = list(args)
+    bad[3] = 0                      # k_mean is required by pack
+    assert L.ulp_pack(*bad, cb, None) == EINVAL
+
+
+def test_unpack_validation(L):
+    def call(B=1, Lq=100, h=2, D=64, P=2, aligned=NONE, ss=NONE):
+        return L.ulp_unpack_for_sage(A, B, Lq, h, D, P, aligned, ss, A, A, A, A, A, None)
+    assert call(aligned=1) == EINVAL and b"aligned=True" in L.ulp_last_error()
+    assert call(aligned=2) == EINVAL
+    assert call(ss=201) == EINVAL and b"scale_sequence" in L.ulp_last_error()
+    assert call(ss=0) == EINVAL
+    assert call(h=0) == EINVAL
+    assert call(D=256) == EUNSUPPORTED
+    assert call(P=5) == EUNSUPPORTED
+    assert L.ulp_unpack_for_sage(A, 1, 128, 2, 64, 2, 1, NONE, A, A, A + 1, A, A, None) == EALIGN
+
+
+def test_group_validation(L):
+    assert L.ulp_group_stats(A, A, 0, 0, 1, 128, 4, 64, 2, NONE, A, A, A, A, None) == EINVAL
+    assert L.ulp_group_derive(A, A, A, A, A, 0, 1, 4, 64, 128, 3, None) == EUNSUPPORTED
+    assert L.ulp_group_pack(A, A, A, A, 0, A, A, 1, 128, 3, 64, 2, A, None) == EINVAL
+    assert L.ulp_group_unpack(A, 1, 100, 2, 64, 2, 1, NONE, A, A, A, A, A, None) == EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """The binding has no fallback: without libulp.so every call raises."""
+    monkeypatch.setattr(ulp, "_lib", None)
+    monkeypatch.setattr(ulp, "LIB_PATH", str(tmp_path / "libulp.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ulp.slots(100)

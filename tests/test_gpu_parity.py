@@ -1,0 +1,278 @@
+"""Parity of the HIP path with the CPU oracle, bit for bit, through the C ABI (GPU).
+
+Every intermediate (boundary min/max, kernel amax, derived amax, chunk bytes) and every
+output (q8, k8, v8, q_scale, k_scale) is compared byte for byte.  The five workloads run in
+the whole-group launch configuration the benchmark times, and through the per-rank entry
+points; the two large ones are compared on sampled heads (one per destination), which the
+oracle computes one by one on the corresponding sub-problem.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import pipeline
+import precision_attention_input_amd as ulp
+from precision_attention_input_amd import workloads as W
+
+from gpu_helpers import (DEV, assert_bits_equal, compare_all, run_group, run_per_rank, say,
+                         sub_heads, to_dev)
+from helpers import small
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_run(w, d, heads=None):
+    if heads is None:
+        return pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                                  used_sequence=w.used, scale_sequence=w.scale_sequence)
+    idx = torch.tensor(heads)
+    sub = {n: d[n][:, :, idx].contiguous() for n in ("Q", "K", "V")}
+    return pipeline.run_group(sub["Q"], sub["K"], sub["V"], d["mean"][:, idx].contiguous(),
+                              world_size=w.P, used_sequence=w.used,
+                              scale_sequence=w.scale_sequence)
+
+
+# ----------------------------------------------------------------- small and medium workloads
+
+@pytest.mark.parametrize("wname", [W.TINY.name, W.UNALIGNED_PADDED.name,
+                                   W.BATCHED_SMALL_HEAD.name])
+@pytest.mark.parametrize("mode", ["group", "per_rank"])
+def test_workload_full_parity(olib, wname, mode):
+    w = W.BY_NAME[wname]
+    say(f"[parity] {wname} mode={mode}")
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    g = run_group(w, dd, aligned=w.aligned) if mode == "group" else run_per_rank(w, dd, w.aligned)
+    ref = oracle_run(w, d)
+    compare_all(g, ref, w, f"{wname}/{mode}")
+
+
+# ----------------------------------------------------------------- large workloads, sampled
+
+_LARGE = {}
+
+
+def large(wname):
+    if wname not in _LARGE:
+        _LARGE.clear()
+        w = W.BY_NAME[wname]
+        say(f"[parity] generating {wname}")
+        d = W.generate(w)
+        _LARGE[wname] = (w, d)
+    return _LARGE[wname]
+
+
+@pytest.mark.parametrize("wname", [W.VIDEO_DIT_ALIGNED.name, W.LONG_UNALIGNED.name])
+def test_large_workload_sampled_heads(olib, wname):
+    w, d = large(wname)
+    heads = W.sample_heads(w, per_dest=1)
+    say(f"[parity] {wname} group launch, sampled heads {heads}")
+    dd = to_dev(d, w.P)
+    g = run_group(w, dd, aligned=w.aligned)
+    ref = oracle_run(w, d, heads)
+    ref.pop("sends")
+    compare_all(sub_heads(g, w, heads), ref, w, f"{wname}/sampled")
+    # the per-rank entry points give the same bytes as the group launch, everywhere
+    say(f"[parity] {wname} per-rank vs group")
+    pr = run_per_rank(w, dd, aligned=w.aligned)
+    for r in range(w.P):
+        assert_bits_equal(pr["k_amax"][r], g["k_amax"][r], f"k_amax r{r}")
+        assert_bits_equal(pr["q_amax"][r], g["q_amax"][r], f"q_amax r{r}")
+    assert_bits_equal(pr["group"], g["group"], "all-to-all buffer")
+    for p in range(w.P):
+        for i in range(5):
+            assert_bits_equal(pr["outs"][p][i], g["outs"][p][i], f"output {i} dest {p}")
+    del dd, g, pr
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------- enumeration of edge shapes
+
+def _edge_cases():
+    cases = []
+    for i, (P, L) in enumerate([(2, 1), (2, 2), (4, 31), (6, 63), (8, 64), (2, 65), (4, 96),
+                                (6, 100), (8, 127), (2, 129), (4, 200), (6, 31), (8, 1),
+                                (2, 384), (4, 1000)]):
+        S = P * L
+        D = (64, 128)[i % 2]
+        dtype = (torch.bfloat16, torch.float16)[(i // 2) % 2]
+        H = P * (1 + i % 3)
+        B = 1 + (i % 2)
+        for used in sorted({S, 1, max(1, S - 1), max(1, (S * 7) // 10)}):
+            ss = used if i % 2 else None
+            cases.append(small(B=B, P=P, L=L, H=H, D=D, dtype=dtype,
+                               used=None if used == S else used, scale_sequence=ss,
+                               seed=500 + i))
+    return cases
+
+
+EDGE = _edge_cases()
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[f"{w.name}_u{w.used}" for w in EDGE])
+def test_edge_shapes(olib, w):
+    say(f"[edge] {w.name} used={w.used} ss={w.scale_sequence}")
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    ref = oracle_run(w, d)
+    compare_all(run_group(w, dd), ref, w, "group")
+    compare_all(run_per_rank(w, dd), ref, w, "per_rank")
+
+
+# ----------------------------------------------------------------- conversions, exhaustively
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_every_input_pattern_through_pack(olib, dtype):
+    """All 65536 16-bit patterns (non-finite ones replaced by 0) as V, Q and K: the E4M3
+    codes, the INT8 codes and the centering all match the oracle."""
+    say(f"[exhaustive] {dtype}")
+    bitsrc = torch.arange(0, 1 << 16, dtype=torch.int32).to(torch.int16).view(dtype)
+    vals = torch.where(torch.isfinite(bitsrc.float()), bitsrc, torch.zeros_like(bitsrc))
+    P, L, H, D = 2, 256, 2, 128                      # 2 * 256 * 2 * 128 = 2 * 65536 elements
+    x = vals.repeat(2).view(1, P * L, H, D)
+    perm = torch.randperm(x.numel(), generator=torch.Generator().manual_seed(3))
+    w = small(P=P, L=L, H=H, D=D, dtype=dtype)
+    d = dict(Q=x.clone(), K=x.flatten()[perm].view_as(x).contiguous(), V=x.clone())
+    d["mean"] = W.k_mean_global(d["K"], P * L, dtype)
+    dd = to_dev(d, P)
+    compare_all(run_group(w, dd), oracle_run(w, d), w, "exhaustive")
+
+
+def test_quantization_ties(olib):
+    """Quotients that are exact half-integers, and the floats next to them, for scales that
+    are powers of two (amax 127 -> scale 1) and for scales that are not."""
+    say("[ties]")
+    P, L, H, D = 2, 128, 2, 64
+    w = small(P=P, L=L, H=H, D=D, dtype=torch.float16)
+    rng = np.random.default_rng(5)
+    Q = np.zeros((1, P * L, H, D), np.float32)
+    for g in range(P * L // 64):
+        amax = [127.0, 100.0, 3.0, 0.0625][g % 4]
+        s = np.float32(amax) / np.float32(127)
+        k = rng.integers(-127, 127, (64, H, D)).astype(np.float32)
+        t = (k + 0.5) * s
+        jitter = rng.choice([-1, 0, 0, 1], (64, H, D))
+        t16 = torch.from_numpy(t).to(torch.float16).float().numpy()
+        ulp16 = np.spacing(np.abs(t16).astype(np.float16)).astype(np.float32)
+        vals = t16 + jitter * ulp16
+        vals[0, 0, 0] = amax
+        vals = np.clip(vals, -amax, amax)
+        Q[0, 64 * g:64 * g + 64] = vals
+    Qt = torch.from_numpy(Q).to(torch.float16)
+    mean = torch.full((1, H, D), 8.0, dtype=torch.float16)
+    d = dict(Q=Qt, K=(Qt.float() + 8.0).to(torch.float16), V=Qt.clone(), mean=mean)
+    dd = to_dev(d, P)
+    compare_all(run_group(w, dd), oracle_run(w, d), w, "ties")
+
+
+# ----------------------------------------------------------------- invariants on the GPU
+
+def test_used_none_equals_used_s_and_aligned_flag(olib):
+    """used None == used S (k_grouped_amax description); aligned True/False/None give the
+    same bytes (unpack_for_sage description)."""
+    w = small(P=4, L=256, H=8, D=128, seed=77)
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    a = run_group(w, dd, aligned=None)
+    b = run_group(w.with_(used=w.S), dd, aligned=True)
+    c = run_group(w, dd, aligned=False)
+    for x in (b, c):
+        for r in range(w.P):
+            assert_bits_equal(x["k_amax"][r], a["k_amax"][r], "k_amax")
+        for p in range(w.P):
+            for i in range(5):
+                assert_bits_equal(x["outs"][p][i], a["outs"][p][i], f"out {i}")
+    with pytest.raises(ValueError, match="aligned=True"):
+        run_group(w.with_(L=200), to_dev(W.generate(w.with_(L=200)), w.P), aligned=True)
+
+
+def test_scale_sequence_prefix_and_determinism(olib):
+    w = W.UNALIGNED_PADDED.with_(B=1, H=8)
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    full = run_group(w.with_(scale_sequence=None), dd)
+    again = run_group(w.with_(scale_sequence=None), dd)
+    for p in range(w.P):
+        for i in range(5):
+            assert_bits_equal(again["outs"][p][i], full["outs"][p][i], "run twice")
+    for ns in (1, 64, 65, 3700, 4000):
+        part = run_group(w.with_(scale_sequence=ns), dd)
+        Wn = (ns + 63) // 64
+        for p in range(w.P):
+            for i in range(3):
+                assert_bits_equal(part["outs"][p][i], full["outs"][p][i], "q/k/v full length")
+            assert_bits_equal(part["outs"][p][3], full["outs"][p][3][..., :Wn], "q_scale prefix")
+            assert_bits_equal(part["outs"][p][4], full["outs"][p][4][..., :Wn], "k_scale prefix")
+
+
+def _guarded(shape, dtype, fill=0xA5):
+    """A tensor of `shape` inside a larger buffer whose margins hold a canary byte."""
+    n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    buf = torch.full((n + 2 * 4096,), fill, dtype=torch.uint8, device=DEV)
+    return buf, buf[4096:4096 + n].view(dtype).view(shape)
+
+
+def _margins_ok(buf, fill=0xA5):
+    m = torch.cat([buf[:4096], buf[-4096:]])
+    return bool((m == fill).all())
+
+
+def test_no_write_outside_outputs(olib):
+    """Every output lives inside a canary-filled buffer: kernels write nothing outside it,
+    and write every byte inside it (no canary survives in an output)."""
+    w = small(B=2, P=4, L=100, H=8, D=64, dtype=torch.float16, used=350, scale_sequence=350,
+              seed=8)
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    P, L, B, H, D = w.P, w.L, w.B, w.H, w.D
+    sl = ulp.slots(L)
+    bufs = {}
+    for name, shape, dt in [("qa", (P, B, H, sl), torch.float32), ("ka", (P, B, H, sl), torch.float32),
+                            ("qm", (P, B, H, 2, 2, D), torch.float32),
+                            ("km", (P, B, H, 2, 2, D), torch.float32)]:
+        bufs[name] = _guarded(shape, dt)
+    ulp.group_stats(dd["Q"], dd["K"], dd["mean"], world_size=P, used_sequence=w.used,
+                    out=tuple(bufs[n][1] for n in ("qa", "ka", "qm", "km")))
+    ulp.group_derive(bufs["qa"][1], bufs["ka"][1], bufs["qm"][1], bufs["km"][1], dd["mean"],
+                     local_sequence=L, world_size=P)
+    cb = ulp.chunk_bytes(B, L, w.h, D)
+    gbuf, grp = _guarded((P, P, cb), torch.uint8)
+    ulp.group_pack(dd["Q"], dd["K"], dd["V"], dd["mean"], bufs["qa"][1], bufs["ka"][1],
+                   world_size=P, group=grp)
+    qk, vs, sc = ulp.unpack_shapes(B, L, w.h, D, P, w.scale_sequence)
+    outs = [_guarded((P, *qk), torch.int8), _guarded((P, *qk), torch.int8),
+            _guarded((P, *vs), torch.uint8), _guarded((P, *sc), torch.float32),
+            _guarded((P, *sc), torch.float32)]
+    views = [o[1] for o in outs]
+    views[2] = views[2].view(torch.float8_e4m3fn)
+    ulp.group_unpack(grp, batch_size=B, local_sequence=L, local_heads=w.h, head_dim=D,
+                     world_size=P, scale_sequence=w.scale_sequence, out=tuple(views))
+    torch.cuda.synchronize()
+    for name, (buf, _) in list(bufs.items()) + [("group", (gbuf, grp))] + \
+            [(f"out{i}", o) for i, o in enumerate(outs)]:
+        assert _margins_ok(buf), f"{name}: write outside the output"
+    ref = oracle_run(w, d)
+    g = dict(q_minmax=bufs["qm"][1], k_minmax=bufs["km"][1],
+             q_amax_kernel=list(ref["q_amax_kernel"]), k_amax_kernel=list(ref["k_amax_kernel"]),
+             q_amax=list(bufs["qa"][1]), k_amax=list(bufs["ka"][1]),
+             sends=[grp[:, r] for r in range(P)],
+             outs={p: tuple(v[p] for v in views) for p in range(P)})
+    compare_all(g, ref, w, "guarded")
+
+
+def test_invalid_arguments_launch_nothing(olib):
+    w = small(P=2, L=100, H=2, D=64)
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    buf, out = _guarded((1, 2, ulp.slots(100)), torch.float32)
+    out.fill_(0)
+    with pytest.raises(ValueError, match="used_sequence"):
+        ulp.k_grouped_amax(dd["K"][0], dd["mean"], rank=0, world_size=2, used_sequence=201,
+                           out=out)
+    with pytest.raises(ValueError, match="rank"):
+        ulp.k_grouped_amax(dd["K"][0], dd["mean"], rank=2, world_size=2, out=out)
+    torch.cuda.synchronize()
+    assert (out == 0).all() and _margins_ok(buf)
