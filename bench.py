@@ -69,6 +69,47 @@ def load_traffic(workload: str, launch_bytes: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _pmc_values(path: str, kernel: str, counter: str) -> list[float]:
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                out.append(float(r["Counter_Value"]))
+    if not out:
+        raise SystemExit(f"{path}: no {counter} rows for {kernel}")
+    return out
+
+
+def record_traffic(args):
+    """Scale the pack kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for a plain device copy of known size, and record the bytes per launch."""
+    from precision_attention_input_amd import workloads as W
+    fk, wk, fc, wc = args.record_traffic
+    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
+    copy_bytes = args.copy_calibration * 2 ** 20
+    if not copy_bytes:
+        raise SystemExit("--record-traffic needs --copy-calibration MIB (the copy's size)")
+    copy_fetch = _pmc_values(fc, "copyBuffer", "FETCH_SIZE")
+    copy_write = _pmc_values(wc, "copyBuffer", "WRITE_SIZE")
+    f_scale = copy_bytes / (1024 * sum(copy_fetch) / len(copy_fetch))
+    w_scale = copy_bytes / (1024 * sum(copy_write) / len(copy_write))
+    kf = _pmc_values(fk, "::pack_kernel<", "FETCH_SIZE")
+    kw = _pmc_values(wk, "::pack_kernel<", "WRITE_SIZE")
+    read = 1024 * sum(kf) / len(kf) * f_scale
+    write = 1024 * sum(kw) / len(kw) * w_scale
+    rec = {"kernel": "pack_kernel", "workload": w.name, "kernel_hash": kernel_hash(),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "hbm_read_bytes_per_launch": round(read), "hbm_write_bytes_per_launch": round(write),
+           "hbm_bytes_per_launch": round(read + write),
+           "algorithmic_bytes_per_launch": algorithmic_bytes(w)["pack"]}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"pack_kernel_{w.name}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, d, reps: int):
     """The CPU oracle's pack+unpack over the whole workload (every rank and destination),
     repeated `reps` times, single-threaded."""
@@ -106,8 +147,19 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
+                    help="kernel FETCH_SIZE csv, kernel WRITE_SIZE csv, copy FETCH_SIZE csv, "
+                         "copy WRITE_SIZE csv (rocprofv3 --pmc counter_collection files of this "
+                         "script's default run and of --copy-calibration): write the pack "
+                         "kernel's scaled HBM bytes per launch under profiles/ and exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB per step (the reference "
+                         "kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args()
 
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (the whole Ulysses group is held "
               f"by one device; world_size only shapes the byte layout); --gpus {args.gpus} "
@@ -119,9 +171,20 @@ def main():
     import precision_attention_input_amd as ulp
     from precision_attention_input_amd import workloads as W
 
-    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "dispatches": args.warmup + args.steps}), flush=True)
+        return
+
+    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
     d = W.generate(w)
     nb = algorithmic_bytes(w)
     set_bytes = 12 * nb["N"]      # stacked Q/K/V (6N) + all-to-all buffer (3N) + outputs (3N)
