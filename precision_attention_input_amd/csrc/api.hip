@@ -51,6 +51,8 @@ int check_shape(const char* fn, int dtype, int64_t B, int64_t L, int64_t H, int6
         return fail(ULP_EINVAL, "%s: batch, local_sequence and heads must be >= 1 "
                                 "(got B=%lld L=%lld H=%lld)", fn, (long long)B, (long long)L,
                     (long long)H);
+    if (H > 65535)
+        return fail(ULP_EINVAL, "%s: at most 65535 heads, got %lld", fn, (long long)H);
     if (H % P != 0)
         return fail(ULP_EINVAL, "%s: heads %lld not divisible by world_size %d", fn,
                     (long long)H, P);
@@ -59,7 +61,7 @@ int check_shape(const char* fn, int dtype, int64_t B, int64_t L, int64_t H, int6
     if (B > lim / L || B * L > lim / H || B * L * H > lim / (D * P))
         return fail(ULP_EINVAL, "%s: problem too large", fn);
     const int64_t slots = ulp::slots_of(L);
-    if (B * slots * ((H + 1) / 2) >= kMaxGrid)
+    if (B * slots * ((H + 1) / 2) >= kMaxGrid || B * ((L + 7) / 8) >= kMaxGrid)
         return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
     return ULP_OK;
 }

@@ -9,16 +9,23 @@
 // local_heads = H / world_size, contiguous per destination).  Chunk sections: q8, k8, v8
 // [B, L, h, D] bytes, then q_scale, k_scale [B, h, slots] fp32, each 256-byte aligned.
 //
-// Work decomposition: one 256-thread workgroup per (rank, b, slot, block of 512 / D heads);
-// a row of the block is 512 elements = 32 threads x 16 elements, so 8 rows are in flight and
-// each thread walks the group's rows with stride 8.  Every thread loads 2 x 16 bytes of each
-// of Q, K and V per row and stores 16 bytes of each code tensor -- fully coalesced on both
-// sides.  The per-group scale and its reciprocal are computed once per thread.
+// Work decomposition: the shard is a [B*L, H*D/16] array of 16-element vectors; one thread
+// owns one vector of each of Q, K and V.  It issues all of its loads first (amax of both
+// tensors, the K mean, 2 x 16 bytes of each of Q, K, V), runs the quantization fast path of
+// all three tensors as straight-line code, stores three 16-byte code vectors, and only then
+// takes the rare exact-quotient fix-up (the near-half-integer test above), which rewrites
+// the 16 codes it affects.  The kernel is VALU-bound, so the per-thread overhead is kept
+// small: 32-bit column arithmetic, one IEEE division and one v_rcp_f32 per tensor.  A
+// 256-thread workgroup covers kRows rows x kCols vectors, so every wave reads and writes
+// whole 1 KB row segments; the grid is (B x row blocks, column blocks, ranks).
 #include "ulp_device.h"
 #include "ulp_kernels.h"
 
 namespace ulp {
 namespace {
+
+constexpr int kCols = 32;                 // 16-element vectors per workgroup row
+constexpr int kRows = kThreads / kCols;   // rows per workgroup
 
 struct PackParams {
     const uint16_t *q, *k, *v, *mean;
@@ -26,7 +33,8 @@ struct PackParams {
     uint8_t* send;
     int64_t dest_stride, x_rank_stride, amax_rank_stride, send_rank_stride;
     int64_t B, L, H, h, P, slots, sec, ssec;
-    int rank0, nhb;
+    uint32_t h_magic;        // floor(x / h) = umulhi(x, h_magic) for x, h < 2^16, h > 1
+    int rank0, nranks, row_blocks;   // row_blocks: per batch entry
 };
 
 template <int DT>
@@ -35,24 +43,67 @@ __device__ __forceinline__ void decode16(const uint4& a, const uint4& b, float* 
     decode8<DT>(b, f + 8);
 }
 
+__device__ __forceinline__ uint4 codes16(const int* c) {
+    return make_uint4(pack_i8x4(c[0], c[1], c[2], c[3]), pack_i8x4(c[4], c[5], c[6], c[7]),
+                      pack_i8x4(c[8], c[9], c[10], c[11]),
+                      pack_i8x4(c[12], c[13], c[14], c[15]));
+}
+
+// 16 inputs held as two raw 16-byte words (K: minus the mean, also two raw words) -> fp32.
+template <int DT, bool CENTER>
+__device__ __forceinline__ void inputs16(const uint4& a, const uint4& b, const uint4& ma,
+                                         const uint4& mb, float* f) {
+    decode16<DT>(a, b, f);
+    if constexpr (CENTER) {
+        float m[16];
+        decode16<DT>(ma, mb, m);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) f[e] = f[e] - m[e];
+    }
+}
+
+// Codes of 16 inputs.  EXACT_ONLY: the division-free exact decision for every value.
+// Otherwise the fast path, falling back to the exact decision when any value of the
+// wave's vectors lies near a half-integer (re-decoding from the raw words keeps few
+// registers live across the fast path).  The exact decision costs about twice the fast
+// path, so it pays to skip the fast path where near-ties are the rule: centered K (small
+// deviations on a coarse grid) and bf16 Q (8-bit significands); see the launch below.
+template <int DT, bool CENTER, bool EXACT_ONLY>
+__device__ __forceinline__ uint4 quantize16(const uint4& a, const uint4& b, const uint4& ma,
+                                            const uint4& mb, const QuantScale& sc) {
+    float f[16];
+    int c[16];
+    inputs16<DT, CENTER>(a, b, ma, mb, f);
+    if constexpr (EXACT_ONLY) {
+        quantize_exact<16>(f, sc, c);
+    } else if (__builtin_expect(!(quantize_fast<16>(f, sc, c) < 0.5f), 0)) {
+        inputs16<DT, CENTER>(a, b, ma, mb, f);
+        quantize_exact<16>(f, sc, c);
+    }
+    return codes16(c);
+}
+
+template <int DT>
+__device__ __forceinline__ uint4 e4m3x16(const uint4& x0, const uint4& x1) {
+    float f[16];
+    decode16<DT>(x0, x1, f);
+    return make_uint4(e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7]),
+                      e4m3x4(f[8], f[9], f[10], f[11]), e4m3x4(f[12], f[13], f[14], f[15]));
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     constexpr int VPH = D / 16;      // 16-element vectors per head row
-    constexpr int HB = 512 / D;      // heads per workgroup
     const int64_t L = p.L, H = p.H, h = p.h;
-    const int64_t rank = p.rank0 + blockIdx.z;
-    uint8_t* send = p.send + blockIdx.z * p.send_rank_stride;
-    int bid = blockIdx.x;
-    const int hb = bid % p.nhb;
-    bid /= p.nhb;
-    const int64_t j = bid % p.slots;
-    const int64_t b = bid / p.slots;
+    const int64_t rz = blockIdx.z;
+    const int64_t rank = p.rank0 + rz;
+    uint8_t* send = p.send + rz * p.send_rank_stride;
     const int tid = threadIdx.x;
 
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
         // Zero the padding bytes after each section of every destination chunk.
-        const int64_t data = p.B * L * h * D;                       // bytes of q8/k8/v8 data
-        const int64_t sdata = 4 * p.B * h * p.slots;                // bytes of scale data
+        const int64_t data = p.B * L * h * D;         // bytes of each code section
+        const int64_t sdata = 4 * p.B * h * p.slots;  // bytes of each scale section
         for (int64_t i = tid; i < p.P * 5 * 256; i += kThreads) {
             const int64_t dst = i / (5 * 256), sect = (i / 256) % 5, off = i % 256;
             const int64_t start = sect < 3 ? sect * p.sec + data
@@ -62,73 +113,62 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
         }
     }
 
-    const int c = tid & 31, rl = tid >> 5;
-    const int hib = c / VPH, dv = c % VPH;
-    const int64_t head = (int64_t)hb * HB + hib;
-    if (head >= H) return;
-    const int64_t dst = head / h, jl = head % h;
-    uint8_t* chunk = send + dst * p.dest_stride;
-    const float* qa = p.q_amax + blockIdx.z * p.amax_rank_stride;
-    const float* ka = p.k_amax + blockIdx.z * p.amax_rank_stride;
-    const QuantScale sq = make_scale(qa[(b * H + head) * p.slots + j]);
-    const QuantScale sk = make_scale(ka[(b * H + head) * p.slots + j]);
-    if (rl == 0 && dv == 0) {
-        float* qs = reinterpret_cast<float*>(chunk + 3 * p.sec);
-        float* ks = reinterpret_cast<float*>(chunk + 3 * p.sec + p.ssec);
-        qs[(b * h + jl) * p.slots + j] = sq.s;
-        ks[(b * h + jl) * p.slots + j] = sk.s;
-    }
+    // Row (b, l) and 16-element column of this thread; rows < 2^31 and columns < 2^20.
+    const uint32_t b = blockIdx.x / (uint32_t)p.row_blocks;
+    const uint32_t l = (blockIdx.x % (uint32_t)p.row_blocks) * kRows + tid / kCols;
+    const uint32_t col = blockIdx.y * kCols + tid % kCols;
+    if (l >= (uint32_t)L || col >= (uint32_t)(H * VPH)) return;
+    const uint32_t head = col / VPH, dv = col % VPH;
+    const uint32_t dst = h == 1 ? head : __umulhi(head, p.h_magic);
+    const uint32_t jl = head - dst * (uint32_t)h;
+    const uint64_t row = (uint64_t)b * (uint64_t)L + l;
+
+    // Issue every load first: amax of both tensors, the K mean, and 2 x 16 bytes of Q, K, V.
+    const uint64_t arow = (uint64_t)rz * p.amax_rank_stride + ((uint64_t)b * H + head) * p.slots;
     const int64_t g0 = first_group(rank, L);
-    const int64_t n = last_group(rank, L) - g0 + 1;
-    if (j >= n) return;
-    const int64_t g = g0 + j;
-    const int64_t lo = max((int64_t)kGroup * g, rank * L) - rank * L;
-    const int64_t hi = min((int64_t)kGroup * g + kGroup, rank * L + L) - rank * L;
+    const int64_t g = (rank * L + l) / kGroup;
+    const uint32_t j = (uint32_t)(g - g0);
+    const float qamax = p.q_amax[arow + j];
+    const float kamax = p.k_amax[arow + j];
+    const uint64_t xo = (uint64_t)rz * p.x_rank_stride + row * (uint64_t)(H * D) + col * 16;
+    const uint4 q0 = load16<ULP_PACK_NT_LOAD>(p.q + xo);
+    const uint4 q1 = load16<ULP_PACK_NT_LOAD>(p.q + xo + 8);
+    const uint4 k0 = load16<ULP_PACK_NT_LOAD>(p.k + xo);
+    const uint4 k1 = load16<ULP_PACK_NT_LOAD>(p.k + xo + 8);
+    const uint4 v0 = load16<ULP_PACK_NT_LOAD>(p.v + xo);
+    const uint4 v1 = load16<ULP_PACK_NT_LOAD>(p.v + xo + 8);
+    const uint16_t* mp = p.mean + ((uint64_t)b * H + head) * D + dv * 16;
+    const uint4 m0 = load16(mp), m1 = load16(mp + 8);
+    // Keep every load above this point: each wave then has all of its reads in flight at
+    // once instead of one tensor's at a time.
+    __builtin_amdgcn_sched_barrier(0);
 
-    float m[16];
-    {
-        const uint16_t* mp = p.mean + (b * H + head) * D + dv * 16;
-        decode16<DT>(load16(mp), load16(mp + 8), m);
-    }
-    const int64_t xoff0 = blockIdx.z * p.x_rank_stride + (b * L * H + head) * D + dv * 16;
-    const int64_t ooff0 = (b * L * h + jl) * D + dv * 16;
-    int8_t* q8 = reinterpret_cast<int8_t*>(chunk);
-    int8_t* k8 = reinterpret_cast<int8_t*>(chunk + p.sec);
-    uint8_t* v8 = chunk + 2 * p.sec;
+    uint8_t* chunk = send + (uint64_t)dst * p.dest_stride;
+    uint8_t* out = chunk + row * (uint64_t)(h * D) + jl * D + dv * 16;
+    const QuantScale sq = make_scale(qamax);
+    const QuantScale sk = make_scale(kamax);
 
-    for (int64_t l = lo + rl; l < hi; l += 8) {
-        const int64_t xo = xoff0 + l * H * D;
-        const uint4 qa0 = load16(p.q + xo), qa1 = load16(p.q + xo + 8);
-        const uint4 ka0 = load16(p.k + xo), ka1 = load16(p.k + xo + 8);
-        const uint4 va0 = load16(p.v + xo), va1 = load16(p.v + xo + 8);
-        float f[16], r[16];
-        uint4 out;
-        const int64_t oo = ooff0 + l * h * D;
+    store16<ULP_PACK_NT_STORE>(out, quantize16<DT, false, DT == kBF16>(q0, q1, m0, m1, sq));
+    store16<ULP_PACK_NT_STORE>(out + p.sec, quantize16<DT, true, true>(k0, k1, m0, m1, sk));
+    store16<ULP_PACK_NT_STORE>(out + 2 * p.sec, e4m3x16<DT>(v0, v1));
 
-        decode16<DT>(qa0, qa1, f);
-        quantize_n<16>(f, sq, r);
-        out.x = pack_i8x4(r[0], r[1], r[2], r[3]);
-        out.y = pack_i8x4(r[4], r[5], r[6], r[7]);
-        out.z = pack_i8x4(r[8], r[9], r[10], r[11]);
-        out.w = pack_i8x4(r[12], r[13], r[14], r[15]);
-        store16(q8 + oo, out);
-
-        decode16<DT>(ka0, ka1, f);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) f[e] = f[e] - m[e];
-        quantize_n<16>(f, sk, r);
-        out.x = pack_i8x4(r[0], r[1], r[2], r[3]);
-        out.y = pack_i8x4(r[4], r[5], r[6], r[7]);
-        out.z = pack_i8x4(r[8], r[9], r[10], r[11]);
-        out.w = pack_i8x4(r[12], r[13], r[14], r[15]);
-        store16(k8 + oo, out);
-
-        decode16<DT>(va0, va1, f);
-        out.x = e4m3x4(f[0], f[1], f[2], f[3]);
-        out.y = e4m3x4(f[4], f[5], f[6], f[7]);
-        out.z = e4m3x4(f[8], f[9], f[10], f[11]);
-        out.w = e4m3x4(f[12], f[13], f[14], f[15]);
-        store16(v8 + oo, out);
+    if (dv == 0) {
+        // The first row of each touched group writes its scales; row 0 also writes the
+        // slots this rank never touches (their amax is passed through like any other).
+        float* qs = reinterpret_cast<float*>(chunk + 3 * p.sec) + ((uint64_t)b * h + jl) * p.slots;
+        float* ks = reinterpret_cast<float*>(chunk + 3 * p.sec + p.ssec) +
+                    ((uint64_t)b * h + jl) * p.slots;
+        if (l == max((int64_t)kGroup * g, rank * L) - rank * L) {
+            qs[j] = sq.s;
+            ks[j] = sk.s;
+        }
+        if (l == 0) {
+            const int64_t n = last_group(rank, L) - g0 + 1;
+            for (int64_t jj = n; jj < p.slots; ++jj) {
+                qs[jj] = p.q_amax[arow + jj] / 127.0f;
+                ks[jj] = p.k_amax[arow + jj] / 127.0f;
+            }
+        }
     }
 }
 
@@ -154,10 +194,13 @@ hipError_t launch_t(const PackLaunch& a, hipStream_t stream) {
     p.slots = slots_of(a.L);
     p.sec = chunk_section(a.B, a.L, p.h, a.D);
     p.ssec = chunk_scale_section(a.B, a.L, p.h);
+    // ceil(2^32 / h); exact floor(x / h) for x, h < 2^16 (unused when h == 1)
+    p.h_magic = p.h > 1 ? (uint32_t)((((uint64_t)1 << 32) + p.h - 1) / p.h) : 0;
     p.rank0 = a.rank0;
-    constexpr int HB = 512 / D;
-    p.nhb = (int)((a.H + HB - 1) / HB);
-    dim3 grid((unsigned)(a.B * p.slots * p.nhb), 1, (unsigned)a.nranks);
+    p.nranks = a.nranks;
+    p.row_blocks = (int)((a.L + kRows - 1) / kRows);
+    const int64_t col_blocks = (a.H * (a.D / 16) + kCols - 1) / kCols;
+    dim3 grid((unsigned)(a.B * p.row_blocks), (unsigned)col_blocks, (unsigned)a.nranks);
     hipLaunchKernelGGL((pack_kernel<DT, D>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

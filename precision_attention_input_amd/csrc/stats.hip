@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t s = lo + rl + 8 * i;
-        v[i] = (valid && s < hi) ? load16(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
+        v[i] = (valid && s < hi) ? load16<ULP_STATS_NT_LOAD>(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
     }
     float acc = -__builtin_inff();
     float mn[8], mx[8];

@@ -51,13 +51,46 @@ __device__ __forceinline__ float decode1(uint16_t b) {
     }
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte global accesses.  NT = true marks the access non-temporal (streamed, not kept in
+// the caches); each kernel picks the policy per tensor (see the ULP_*_NT switches below).
+template <bool NT = false>
 __device__ __forceinline__ uint4 load16(const void* p) {
-    return *reinterpret_cast<const uint4*>(p);
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void store16(void* p, const uint4& v) {
-    *reinterpret_cast<uint4*>(p) = v;
+    if constexpr (NT) {
+        const u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+    } else {
+        *reinterpret_cast<uint4*>(p) = v;
+    }
 }
+
+// Cache policy per kernel and direction (1 = non-temporal).
+#ifndef ULP_STATS_NT_LOAD
+#define ULP_STATS_NT_LOAD 1
+#endif
+#ifndef ULP_PACK_NT_LOAD
+#define ULP_PACK_NT_LOAD 0
+#endif
+#ifndef ULP_PACK_NT_STORE
+#define ULP_PACK_NT_STORE 1
+#endif
+#ifndef ULP_UNPACK_NT_LOAD
+#define ULP_UNPACK_NT_LOAD 1
+#endif
+#ifndef ULP_UNPACK_NT_STORE
+#define ULP_UNPACK_NT_STORE 1
+#endif
 
 // min(max(x, lo), hi) in one v_med3_f32 for finite lo <= hi.
 __device__ __forceinline__ float clampf(float x, float lo, float hi) {
@@ -85,47 +118,85 @@ __device__ __forceinline__ float wave_min_xor(float v) {
 //
 // code = clamp(rint(RN(x / s)), -127, 127) with RN(x / s) the IEEE quotient.
 //
-// Fast path: with y = RN(1/s), t = RN(x * y) satisfies |t - RN(x/s)| <= (3u + u^2)/(1-2u-u^2)
-// |t| < 2^-21 |t| (u = 2^-24): y carries relative error <= u, the product adds <= u, and
-// RN(x/s) is within u of x/s.  So whenever t lies farther than 2^-21 |t| from every
-// half-integer, RN(x/s) lies strictly on the same side of every half-integer as t and
-// rint gives the same integer.  Only the rare t close to a half-integer needs the true
-// quotient.  Quotients are first clamped to [-128, 128]; every value beyond rounds and
-// clamps to +-127 either way.
+// Fast path: t = RN(x * y) with y the hardware reciprocal of s.  v_rcp_f32 is within 1 ulp
+// of the correctly rounded reciprocal (checked on gfx950 for every mantissa), so with
+// u = 2^-24, |y - 1/s| <= 1.5 ulp <= 3u/s.  Then |x*y - x/s| <= 3u|x/s|, the product's
+// rounding adds <= u(1+3u)|x/s|, and RN(x/s) is within u|x/s| of x/s, so
+//   |t - RN(x/s)| <= (5u + 3u^2) |x/s| <= (5u + 3u^2) / (1 - 4u - 3u^2) |t| < 2^-21 |t|.
+// Whenever t lies farther than 2^-21 |t| from every half-integer, RN(x/s) lies strictly on
+// the same side of every half-integer as t and rint gives the same integer.  Only the rare
+// t close to a half-integer needs the true quotient (checked per 16 values, fixed after the
+// fast-path codes are stored).
+//
+// Clamping the quotient to [-127, 127] before rint is the same as clamping the rounded
+// integer afterwards (the bounds are integers and rint is monotone), and a clamped t sits
+// exactly on an integer, so the near-half-integer test never fires for it.  The test is
+// |t - rint(t)| + 2^-21 |t| >= 1/2, one fma per value (the product by 2^-21 is exact).
 struct QuantScale {
-    float s;   // the stored fp32 scale
-    float y;   // RN(1 / s)
+    float s;     // the stored fp32 scale, RN(amax / 127)
+    float y;     // reciprocal of s within 1 ulp
+    float s24;   // s * 2^-24 (exact)
 };
 
 __device__ __forceinline__ QuantScale make_scale(float amax) {
     QuantScale q;
-    q.s = amax / 127.0f;     // IEEE division (correctly rounded)
-    q.y = 1.0f / q.s;
+    q.s = amax / 127.0f;                     // IEEE division (correctly rounded)
+    q.y = __builtin_amdgcn_rcpf(q.s);        // s >= 1e-7/127 is normal: no denormal issue
+    q.s24 = q.s * 0x1p-24f;
     return q;
 }
 
-// Quantize N values; returns the rounded (not yet clamped to +-127) quotients in r.
+// Fast path over N values: int8 codes (as int) in c; returns the largest
+// |t - rint(t)| + 2^-21 |t| (>= 0.5 means some value needs the exact decision).
 template <int N>
-__device__ __forceinline__ void quantize_n(const float* x, const QuantScale& qs, float* r) {
-    bool near = false;
+__device__ __forceinline__ float quantize_fast(const float* x, const QuantScale& qs, int* c) {
+    float worst = 0.0f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        float t = clampf(x[i] * qs.y, -128.0f, 128.0f);
-        r[i] = __builtin_rintf(t);
-        near |= (__builtin_fabsf(t - r[i]) + __builtin_fabsf(t) * 0x1p-21f) >= 0.5f;
+        const float t = clampf(x[i] * qs.y, -127.0f, 127.0f);
+        const float r = __builtin_rintf(t);
+        c[i] = (int)r;
+        worst = fmaxf(worst, __builtin_fmaf(__builtin_fabsf(t), 0x1p-21f, __builtin_fabsf(t - r)));
     }
-    if (__builtin_expect(near, 0)) {
+    return worst;
+}
+
+// Exact decision without a division: clamp(rint(RN(x/s)), -127, 127) for any x.
+//
+// Let k = floor(t) for t = x*y clamped to [-127.25, 127.25], and h = k + 1/2.  Because t is
+// within 2^-21 |t| of RN(x/s), rint(RN(x/s)) is k if RN(x/s) < h, k+1 if RN(x/s) > h, and
+// the even one of the two if RN(x/s) == h (values clamped at +-127.25 end at +-127 in every
+// case).  h has at most 9 significant bits, so its last significand bit is 0: its float
+// neighbours are h -+ 2e with e = ulp(h)/2, and a quotient exactly on a midpoint h -+ e rounds
+// to h.  (For |h| = 1/2 the midpoint toward zero is at e/2, but there both outcomes on that
+// side give the same code, 0.)  So RN(x/s) == h  <=>  |x - s*h| <= s*e, and the sign of
+// x - s*h orders x/s against h.  D = fma(-s, h, x) is x - s*h exactly whenever |x - s*h| is
+// near s*e: x and s*h are then multiples of a common power of two at most 2^13 times smaller
+// than |D|, so D needs at most 13 significant bits; elsewhere D still has the right sign and
+// lies far from +-s*e.  s*e = (s * 2^-24) * 2^exponent(h) is exact.
+template <int N>
+__device__ __forceinline__ void quantize_exact(const float* x, const QuantScale& qs, int* c) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) r[i] = __builtin_rintf(clampf(x[i] / qs.s, -128.0f, 128.0f));
+    for (int i = 0; i < N; ++i) {
+        const float t = clampf(x[i] * qs.y, -127.25f, 127.25f);
+        const float k = __builtin_floorf(t);
+        const float h = k + 0.5f;
+        const float d = __builtin_fmaf(-qs.s, h, x[i]);
+        const float e = qs.s24 * __uint_as_float(__float_as_uint(h) & 0x7f800000u);
+        const int ki = (int)k;
+        const int inc = d > e ? 1 : (__builtin_fabsf(d) <= e ? (ki & 1) : 0);
+        c[i] = min(max(ki + inc, -127), 127);
     }
 }
 
-// Four rounded quotients -> four int8 codes packed little-endian in a dword.
-__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
-    uint32_t ia = (uint32_t)(int)clampf(a, -127.0f, 127.0f);
-    uint32_t ib = (uint32_t)(int)clampf(b, -127.0f, 127.0f);
-    uint32_t ic = (uint32_t)(int)clampf(c, -127.0f, 127.0f);
-    uint32_t id = (uint32_t)(int)clampf(d, -127.0f, 127.0f);
+template <int N>
+__device__ __forceinline__ void quantize_n(const float* x, const QuantScale& qs, int* c) {
+    if (__builtin_expect(!(quantize_fast<N>(x, qs, c) < 0.5f), 0)) quantize_exact<N>(x, qs, c);
+}
+
+// Four int8 codes (held as int in [-127, 127]) packed little-endian in a dword.
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+    const uint32_t ia = (uint32_t)a, ib = (uint32_t)b, ic = (uint32_t)c, id = (uint32_t)d;
     // byte 0 of each: selector 0x0c yields a zero byte
     uint32_t lo = __builtin_amdgcn_perm(ib, ia, 0x0c0c0400u);   // [a0, b0, 0, 0]
     uint32_t hi = __builtin_amdgcn_perm(id, ic, 0x04000c0cu);   // [0, 0, c0, d0]

@@ -20,7 +20,10 @@
 namespace ulp {
 namespace {
 
-constexpr int kCopyUnroll = 4;
+#ifndef ULP_UNPACK_COPY_UNROLL
+#define ULP_UNPACK_COPY_UNROLL 4
+#endif
+constexpr int kCopyUnroll = ULP_UNPACK_COPY_UNROLL;
 
 struct UnpackParams {
     const uint8_t* recv;
@@ -51,12 +54,12 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
 #pragma unroll
         for (int i = 0; i < kCopyUnroll; ++i) {
             const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) v[i] = load16(src + 16 * e);
+            if (e < p.seg_vecs) v[i] = load16<ULP_UNPACK_NT_LOAD>(src + 16 * e);
         }
 #pragma unroll
         for (int i = 0; i < kCopyUnroll; ++i) {
             const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) store16(dst + 16 * e, v[i]);
+            if (e < p.seg_vecs) store16<ULP_UNPACK_NT_STORE>(dst + 16 * e, v[i]);
         }
         return;
     }
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (t0 + i < p.S) x = load16(vsec + s * p.cb + l * h * D);
+            if (t0 + i < p.S) x = load16<ULP_UNPACK_NT_LOAD>(vsec + s * p.cb + l * h * D);
             w[i][0] = x.x;
             w[i][1] = x.y;
             w[i][2] = x.z;
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         uint8_t* out = p.v8 + z * p.v_dest_stride + ((b * D + d0) * h + j) * p.spad + t0;
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc)
-            store16(out + (int64_t)cc * h * p.spad, make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
+            store16<ULP_UNPACK_NT_STORE>(out + (int64_t)cc * h * p.spad, make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
         return;
     }
     bid -= p.n_v;

@@ -168,6 +168,41 @@ def test_quantization_ties(olib):
     compare_all(run_group(w, dd), oracle_run(w, d), w, "ties")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_quantization_many_scales(olib, dtype):
+    """Every 64-row group gets its own amax, spread over many binades, and values at, next to
+    and between the half-integer multiples of amax/127: the fast path and the exact decision
+    are both exercised across scales (bf16 and fp16 inputs, raw Q and centered K)."""
+    say(f"[scales] {dtype}")
+    P, L, H, D = 2, 1024, 2, 64
+    w = small(P=P, L=L, H=H, D=D, dtype=dtype)
+    rng = np.random.default_rng(11)
+    S = P * L
+    G = S // 64
+    lo, hi = (-20, 12) if dtype == torch.bfloat16 else (-10, 10)
+    Q = np.zeros((1, S, H, D), np.float32)
+    for g in range(G):
+        for hh in range(H):
+            amax = float(torch.tensor(rng.uniform(1, 2) * 2.0 ** rng.integers(lo, hi))
+                         .to(dtype).float())
+            n = 64 * D
+            k = rng.integers(-127, 127, n)
+            ties = (k + 0.5) * amax / 127.0
+            kind = rng.integers(0, 4, n)
+            vals = np.where(kind == 0, ties,
+                   np.where(kind == 1, ties * (1 + rng.choice([-1, 1], n) * 2.0 ** -9),
+                   np.where(kind == 2, rng.uniform(-amax, amax, n),
+                            np.round(rng.uniform(-127, 127, n)) * amax / 127.0)))
+            vals = torch.from_numpy(vals).float().to(dtype).float().clamp(-amax, amax).numpy()
+            vals[0] = amax
+            Q[0, 64 * g:64 * g + 64, hh] = vals.reshape(64, D)
+    Qt = torch.from_numpy(Q).to(dtype)
+    mean = torch.full((1, H, D), 0.75, dtype=dtype)
+    d = dict(Q=Qt, K=(Qt.float() + 0.75).to(dtype), V=Qt.clone(), mean=mean)
+    dd = to_dev(d, P)
+    compare_all(run_group(w, dd), oracle_run(w, d), w, "many scales")
+
+
 # ----------------------------------------------------------------- invariants on the GPU
 
 def test_used_none_equals_used_s_and_aligned_flag(olib):
