@@ -91,7 +91,7 @@ __device__ __forceinline__ uint4 e4m3x16(const uint4& x0, const uint4& x1) {
                       e4m3x4(f[8], f[9], f[10], f[11]), e4m3x4(f[12], f[13], f[14], f[15]));
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NT>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     constexpr int VPH = D / 16;      // 16-element vectors per head row
     const int64_t L = p.L, H = p.H, h = p.h;
@@ -131,12 +131,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     const float qamax = p.q_amax[arow + j];
     const float kamax = p.k_amax[arow + j];
     const uint64_t xo = (uint64_t)rz * p.x_rank_stride + row * (uint64_t)(H * D) + col * 16;
-    const uint4 q0 = load16<ULP_PACK_NT_LOAD>(p.q + xo);
-    const uint4 q1 = load16<ULP_PACK_NT_LOAD>(p.q + xo + 8);
-    const uint4 k0 = load16<ULP_PACK_NT_LOAD>(p.k + xo);
-    const uint4 k1 = load16<ULP_PACK_NT_LOAD>(p.k + xo + 8);
-    const uint4 v0 = load16<ULP_PACK_NT_LOAD>(p.v + xo);
-    const uint4 v1 = load16<ULP_PACK_NT_LOAD>(p.v + xo + 8);
+    const uint4 q0 = load16(p.q + xo);
+    const uint4 q1 = load16(p.q + xo + 8);
+    const uint4 k0 = load16(p.k + xo);
+    const uint4 k1 = load16(p.k + xo + 8);
+    const uint4 v0 = load16(p.v + xo);
+    const uint4 v1 = load16(p.v + xo + 8);
     const uint16_t* mp = p.mean + ((uint64_t)b * H + head) * D + dv * 16;
     const uint4 m0 = load16(mp), m1 = load16(mp + 8);
     // Keep every load above this point: each wave then has all of its reads in flight at
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     const QuantScale sq = make_scale(qamax);
     const QuantScale sk = make_scale(kamax);
 
-    store16<ULP_PACK_NT_STORE>(out, quantize16<DT, false, DT == kBF16>(q0, q1, m0, m1, sq));
-    store16<ULP_PACK_NT_STORE>(out + p.sec, quantize16<DT, true, true>(k0, k1, m0, m1, sk));
-    store16<ULP_PACK_NT_STORE>(out + 2 * p.sec, e4m3x16<DT>(v0, v1));
+    store16<NT>(out, quantize16<DT, false, DT == kBF16>(q0, q1, m0, m1, sq));
+    store16<NT>(out + p.sec, quantize16<DT, true, true>(k0, k1, m0, m1, sk));
+    store16<NT>(out + 2 * p.sec, e4m3x16<DT>(v0, v1));
 
     if (dv == 0) {
         // The first row of each touched group writes its scales; row 0 also writes the
@@ -201,7 +201,11 @@ hipError_t launch_t(const PackLaunch& a, hipStream_t stream) {
     p.row_blocks = (int)((a.L + kRows - 1) / kRows);
     const int64_t col_blocks = (a.H * (a.D / 16) + kCols - 1) / kCols;
     dim3 grid((unsigned)(a.B * p.row_blocks), (unsigned)col_blocks, (unsigned)a.nranks);
-    hipLaunchKernelGGL((pack_kernel<DT, D>), grid, dim3(kThreads), 0, stream, p);
+    const int64_t written = a.nranks * 3 * a.B * a.L * a.H * a.D;   // code bytes of this launch
+    if (written > kResidentBytes)
+        hipLaunchKernelGGL((pack_kernel<DT, D, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((pack_kernel<DT, D, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ struct StatsParams {
     int boundary_only;            // grid covers slot 0 and slot n-1 only (min/max alone)
 };
 
-template <int DT, int D>
+template <int DT, int D, bool NT>
 __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
     constexpr int VPH = D / 8;       // 16-byte vectors per head row
     constexpr int HB = 256 / D;      // heads per workgroup: 32 vectors per row
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t s = lo + rl + 8 * i;
-        v[i] = (valid && s < hi) ? load16<ULP_STATS_NT_LOAD>(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
+        v[i] = (valid && s < hi) ? load16<NT>(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
     }
     float acc = -__builtin_inff();
     float mn[8], mx[8];
@@ -189,7 +189,11 @@ hipError_t launch_t(const StatsLaunch& a, hipStream_t stream) {
     p.boundary_only = any_amax ? 0 : 1;
     p.grid_slots = any_amax ? (int)p.slots : 2;
     dim3 grid((unsigned)(a.B * p.grid_slots * p.nhb), a.x[1] ? 2 : 1, (unsigned)a.nranks);
-    hipLaunchKernelGGL((stats_kernel<DT, D>), grid, dim3(kThreads), 0, stream, p);
+    const int64_t streamed = (a.x[1] ? 2 : 1) * a.nranks * a.B * a.L * a.H * D * 2;
+    if (streamed > kResidentBytes)
+        hipLaunchKernelGGL((stats_kernel<DT, D, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((stats_kernel<DT, D, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

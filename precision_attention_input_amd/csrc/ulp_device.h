@@ -54,7 +54,7 @@ __device__ __forceinline__ float decode1(uint16_t b) {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // 16-byte global accesses.  NT = true marks the access non-temporal (streamed, not kept in
-// the caches); each kernel picks the policy per tensor (see the ULP_*_NT switches below).
+// the caches); each launcher picks the policy from the size of its streams (see below).
 template <bool NT = false>
 __device__ __forceinline__ uint4 load16(const void* p) {
     if constexpr (NT) {
@@ -75,22 +75,13 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
     }
 }
 
-// Cache policy per kernel and direction (1 = non-temporal).
-#ifndef ULP_STATS_NT_LOAD
-#define ULP_STATS_NT_LOAD 1
-#endif
-#ifndef ULP_PACK_NT_LOAD
-#define ULP_PACK_NT_LOAD 0
-#endif
-#ifndef ULP_PACK_NT_STORE
-#define ULP_PACK_NT_STORE 1
-#endif
-#ifndef ULP_UNPACK_NT_LOAD
-#define ULP_UNPACK_NT_LOAD 1
-#endif
-#ifndef ULP_UNPACK_NT_STORE
-#define ULP_UNPACK_NT_STORE 1
-#endif
+// Cache policy.  A stream whose bytes fit comfortably in the 256 MB last-level cache
+// (Infinity Cache) is read and written with the default policy, so the next kernel of the
+// step finds it there (the pack re-reads Q and K right after the statistics pass; the
+// unpack reads the chunks the pack just wrote).  Larger streams cannot stay resident, and
+// non-temporal accesses then keep them from evicting data that can; the launchers pick the
+// instantiation from the stream's size.
+constexpr int64_t kResidentBytes = (int64_t)128 << 20;
 
 // min(max(x, lo), hi) in one v_med3_f32 for finite lo <= hi.
 __device__ __forceinline__ float clampf(float x, float lo, float hi) {

@@ -36,7 +36,7 @@ struct UnpackParams {
     int64_t copy_bps, n_copy, n_v, v_tiles;
 };
 
-template <int D>
+template <int D, bool NT>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
     const int64_t z = blockIdx.z;
     const uint8_t* recv = p.recv + z * p.recv_dest_stride;
@@ -54,12 +54,12 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
 #pragma unroll
         for (int i = 0; i < kCopyUnroll; ++i) {
             const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) v[i] = load16<ULP_UNPACK_NT_LOAD>(src + 16 * e);
+            if (e < p.seg_vecs) v[i] = load16<true>(src + 16 * e);
         }
 #pragma unroll
         for (int i = 0; i < kCopyUnroll; ++i) {
             const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) store16<ULP_UNPACK_NT_STORE>(dst + 16 * e, v[i]);
+            if (e < p.seg_vecs) store16<NT>(dst + 16 * e, v[i]);
         }
         return;
     }
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (t0 + i < p.S) x = load16<ULP_UNPACK_NT_LOAD>(vsec + s * p.cb + l * h * D);
+            if (t0 + i < p.S) x = load16<true>(vsec + s * p.cb + l * h * D);
             w[i][0] = x.x;
             w[i][1] = x.y;
             w[i][2] = x.z;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         uint8_t* out = p.v8 + z * p.v_dest_stride + ((b * D + d0) * h + j) * p.spad + t0;
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc)
-            store16<ULP_UNPACK_NT_STORE>(out + (int64_t)cc * h * p.spad, make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
+            store16<NT>(out + (int64_t)cc * h * p.spad, make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
         return;
     }
     bid -= p.n_v;
@@ -152,7 +152,13 @@ hipError_t launch_t(const UnpackLaunch& a, hipStream_t stream) {
     p.n_v = (a.B * a.h * p.v_tiles + 3) / 4;
     const int64_t n_scale = (a.B * a.h * a.W + kThreads - 1) / kThreads;
     dim3 grid((unsigned)(p.n_copy + p.n_v + n_scale), 1, (unsigned)a.ndests);
-    hipLaunchKernelGGL((unpack_kernel<D>), grid, dim3(kThreads), 0, stream, p);
+    // the received chunks are read once (non-temporal); outputs stay cached when small, for
+    // the consumer that reads them next
+    const int64_t written = a.ndests * (2 * a.B * p.S * a.h * D + a.B * D * a.h * p.spad);
+    if (written > kResidentBytes)
+        hipLaunchKernelGGL((unpack_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((unpack_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
