@@ -9,7 +9,8 @@ each step reads data last touched several steps earlier (the sets together excee
 
 The reported value is pack+unpack algorithmic bytes / pack+unpack kernel time (HIP events
 around those launches in every timed step); the statistics kernel is reported beside it
-(amax GB/s).  Prints one JSON line.
+(amax GB/s), and the global K mean (an input of the step, timed in its own loop after the
+steps) as k_mean GB/s.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -45,7 +46,10 @@ def algorithmic_bytes(w) -> dict:
     # fused statistics: read Q and K once, the mean per rank; write both amax tensors and
     # both boundary min/max tensors
     stats = 2 * e * N + P * e * B * H * D + 2 * 4 * B * H * sigma * P + 2 * 4 * P * B * H * 4 * D
-    return dict(pack=pack, unpack=unpack, stats=stats, N=N)
+    # global K mean: read the live rows of K once, write the binary32 and dtype means
+    used = w.used or S
+    k_mean = e * B * used * H * D + (4 + e) * B * H * D
+    return dict(pack=pack, unpack=unpack, stats=stats, k_mean=k_mean, N=N)
 
 
 def kernel_hash() -> str:
@@ -237,6 +241,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # The global K mean, an input of the step (formed once per K tensor), timed on its own.
+    ws = torch.empty(int(ulp.lib().ulp_k_mean_workspace_bytes(B, L, H, D, P, ulp._none(w.used))),
+                     dtype=torch.uint8, device=dev)
+    km_out = (torch.empty(B, H, D, dtype=torch.float32, device=dev),
+              torch.empty(B, H, D, dtype=w.dtype, device=dev))
+    for i in range(args.warmup):
+        ulp.k_mean(sets[i % nsets]["K"], world_size=P, used_sequence=w.used, workspace=ws,
+                   out=km_out)
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for i in range(K):
+        kev[i][0].record()
+        ulp.k_mean(sets[i % nsets]["K"], world_size=P, used_sequence=w.used, workspace=ws,
+                   out=km_out)
+        kev[i][1].record()
+    torch.cuda.synchronize()
+    k_mean_ms = sum(e[0].elapsed_time(e[1]) for e in kev) / K
+
     stats_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     derive_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
     pack_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
@@ -281,6 +302,8 @@ def main():
         "stats_ms": round(stats_ms, 5),
         "derive_ms": round(derive_ms, 5),
         "amax_gbps": round(nb["stats"] / (stats_ms * 1e-3) / 1e9, 2),
+        "k_mean_ms": round(k_mean_ms, 5),
+        "k_mean_gbps": round(nb["k_mean"] / (k_mean_ms * 1e-3) / 1e9, 2),
         "step_gbps": round((pu_bytes + nb["stats"]) / (ms_per_step * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

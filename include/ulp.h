@@ -185,6 +185,33 @@ int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int6
                      int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
                      int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * The global K mean (the input k_mean_global of the k_grouped_amax and
+ * derive_k_boundary_amax pages, Parameters: a contiguous [B, H, D] mean of K, rounded to the
+ * input dtype).  Formed over the live rows [0, used) of the whole sequence from the stacked
+ * shards [P, B, L, H, D]: a binary64 sum, divided by used in binary64, rounded to binary32
+ * (mean_f32) and from binary32 to the dtype by round-to-nearest-even (mean_dtype).  The
+ * reduction order is fixed, so results are reproducible run to run; the binary32 mean is
+ * within a relative 1e-6 of the exact mean (in practice equal to the correctly rounded
+ * binary64 result).  On several GPUs each rank would sum its own rows and one all-reduce of
+ * the [B, H, D] binary64 sums would precede the division.
+ * --------------------------------------------------------------------------------- */
+
+/* Bytes of workspace ulp_k_mean needs: 8 * B * H * D * ceil(used / R), used = S when
+ * used_sequence is ULP_NONE, with R in {32, 64, ..., 512} chosen from the shape (at most
+ * 8 * B * H * D * ceil(used / 32)).  0 when an argument is out of range. */
+int64_t ulp_k_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D, int world_size,
+                                   int64_t used_sequence);
+
+/*   k           [P, B, L, H, D] dtype, stacked shards.
+ *   workspace   device memory of at least ulp_k_mean_workspace_bytes() bytes, owned by the
+ *               caller; its contents on entry do not matter.
+ *   mean_f32    [B, H, D] float.
+ *   mean_dtype  [B, H, D] dtype, or NULL when only the binary32 mean is wanted. */
+int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+               int world_size, int64_t used_sequence, void* workspace, int64_t workspace_bytes,
+               float* mean_f32, void* mean_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

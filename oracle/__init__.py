@@ -67,6 +67,12 @@ def _load(path: str = LIB_PATH):
     lib.ora_pack.restype = None
     lib.ora_unpack_for_sage.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.ora_unpack_for_sage.restype = None
+    lib.ora_bf16_bits.argtypes = [ctypes.c_float]
+    lib.ora_bf16_bits.restype = ctypes.c_uint16
+    lib.ora_fp16_bits.argtypes = [ctypes.c_float]
+    lib.ora_fp16_bits.restype = ctypes.c_uint16
+    lib.ora_k_mean.argtypes = [vp, i32, i64, i64, i64, i64, i64, i64, vp, vp]
+    lib.ora_k_mean.restype = None
     return lib
 
 
@@ -173,3 +179,20 @@ def unpack_for_sage(recv, *, batch_size, local_sequence, local_heads, head_dim, 
     lb.ora_unpack_for_sage(_p(recv.contiguous()), B, L, h, D, P, scale_sequence or 0,
                            _p(q8), _p(k8), _p(v8), _p(qs), _p(ks))
     return q8, k8, v8, qs, ks
+
+
+def dtype_bits(x: float, dtype) -> int:
+    """binary32 value -> 16-bit pattern of bf16/fp16, round to nearest even."""
+    f = lib().ora_bf16_bits if dtype == torch.bfloat16 else lib().ora_fp16_bits
+    return int(f(x))
+
+
+def k_mean(k_stack, *, used_sequence=None, _lib=None):
+    """k_stack: stacked shards [P,B,L,H,D] -> (mean fp32 [B,H,D], mean in the dtype)."""
+    lb = _lib or lib()
+    P, B, L, H, D = k_stack.shape
+    mf = torch.empty(B, H, D, dtype=torch.float32)
+    md = torch.empty(B, H, D, dtype=k_stack.dtype)
+    lb.ora_k_mean(_p(k_stack.contiguous()), _dt(k_stack), B, L, H, D, P, used_sequence or 0,
+                  _p(mf), _p(md))
+    return mf, md

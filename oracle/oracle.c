@@ -21,6 +21,9 @@
  *                               Parameters name the [world_size, chunk_bytes] buffer).
  *   ora_unpack_for_sage         flashinfer.comm._ulysses_lowp.unpack_for_sage (description,
  *                               Returns).
+ *   ora_k_mean                  the global K mean the pages take as an input already rounded
+ *                               to the dtype (k_grouped_amax Parameters, k_mean_global): a
+ *                               binary64 mean over the live rows, then binary32, then dtype.
  *
  * Floating point: build with -O2 -ffp-contract=off and without -ffast-math on x86-64
  * (SSE arithmetic, FLT_EVAL_METHOD 0): every float operation below is a single IEEE
@@ -318,5 +321,59 @@ void ora_unpack_for_sage(const uint8_t* recv, int64_t B, int64_t L, int64_t h, i
                 memcpy(&kv, chunk + 3 * sec + ssec + 4 * ((b * h + j) * slots + sl), 4);
                 q_scale[(b * h + j) * W + g] = qv;
                 k_scale[(b * h + j) * W + g] = kv;
+            }
+}
+
+/* ------------------------------------------------------------------ the global K mean */
+
+/* binary32 -> bfloat16 bits, round to nearest even (finite inputs). */
+uint16_t ora_bf16_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lsb = (u >> 16) & 1;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/* binary32 -> IEEE binary16 bits, round to nearest even, overflow to infinity, gradual
+ * underflow (finite inputs).  Written from the format: 5 exponent bits (bias 15),
+ * 10 fraction bits, subnormal step 2^-24. */
+uint16_t ora_fp16_bits(float f) {
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    float a = fabsf(f);
+    if (a >= 65520.0f) return sign | 0x7C00;          /* rounds past the largest, 65504 */
+    if (a < 0x1p-14f) {                               /* subnormal range (and zero) */
+        float n = rintf(ldexpf(a, 24));               /* multiples of 2^-24; 1024 -> 2^-14 */
+        return sign | (uint16_t)n;
+    }
+    int e2;
+    frexpf(a, &e2);                                   /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    float n = rintf(ldexpf(a, 10 - E));               /* in [1024, 2048] */
+    if (n == 2048.0f) {
+        E += 1;
+        n = 1024.0f;
+    }
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)n - 1024));
+}
+
+/* The global K mean over the live rows [0, used) of the stacked shards k [P,B,L,H,D]:
+ * a binary64 sum in row order, divided by used in binary64, rounded to binary32
+ * (mean_f32 [B,H,D]) and from there to the input dtype (mean_dt [B,H,D], 16-bit patterns). */
+void ora_k_mean(const uint16_t* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+                int64_t P, int64_t used, float* mean_f32, uint16_t* mean_dt) {
+    int64_t S = P * L;
+    int64_t u = used > 0 ? used : S;
+    for (int64_t b = 0; b < B; b++)
+        for (int64_t hh = 0; hh < H; hh++)
+            for (int64_t d = 0; d < D; d++) {
+                double sum = 0.0;
+                for (int64_t t = 0; t < u; t++) {
+                    int64_t r = t / L, l = t % L;
+                    sum += (double)elem(k, (((r * B + b) * L + l) * H + hh) * D + d, dtype);
+                }
+                float m = (float)(sum / (double)u);
+                mean_f32[(b * H + hh) * D + d] = m;
+                mean_dt[(b * H + hh) * D + d] = dtype == ORA_BF16 ? ora_bf16_bits(m)
+                                                                  : ora_fp16_bits(m);
             }
 }

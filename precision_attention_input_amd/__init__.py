@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
-    "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer",
+    "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
     "unpack_shapes",
 ]
 
@@ -68,6 +68,8 @@ def lib():
                                i32),
             "ulp_group_unpack": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp],
                                  i32),
+            "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
+            "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -275,3 +277,23 @@ def group_unpack(group, *, batch_size, local_sequence, local_heads, head_dim, wo
                                   head_dim, world_size, _none(aligned), _none(scale_sequence),
                                   _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _stream(group)))
     return tuple(out)
+
+
+# ------------------------------------------------------------------------- global K mean
+
+def k_mean(k, *, world_size, used_sequence=None, workspace=None, out=None):
+    """Stacked K shards [P,B,L,H,D] -> (mean fp32 [B,H,D], mean in the dtype [B,H,D]): the
+    k_mean_global input of the pages, over the live rows [0, used)."""
+    P, B, L, H, D = k.shape
+    need = int(lib().ulp_k_mean_workspace_bytes(B, L, H, D, world_size, _none(used_sequence)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k.device)
+    if out is None:
+        out = (torch.empty(B, H, D, dtype=torch.float32, device=k.device),
+               torch.empty(B, H, D, dtype=k.dtype, device=k.device))
+    _dev(k, workspace, *out)
+    mf, md = out
+    _check(lib().ulp_k_mean(_p(k), _dt(k), B, L, H, D, world_size, _none(used_sequence),
+                            _p(workspace), workspace.numel() * workspace.element_size(),
+                            _p(mf), _p(md), _stream(k)))
+    return mf, md

@@ -345,4 +345,40 @@ int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int6
                          scale_sequence, q8, k8, v8, q_scale, k_scale, world_size, stream);
 }
 
+int64_t ulp_k_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D, int world_size,
+                                   int64_t used_sequence) {
+    if (B < 1 || L < 1 || H < 1 || D < 1 || world_size < 1) return 0;
+    const int64_t S = (int64_t)world_size * L;
+    if (used_sequence != ULP_NONE && (used_sequence < 1 || used_sequence > S)) return 0;
+    return 8 * B * H * D * ulp::kmean_chunks(B, H, D, used_or_s(used_sequence, S));
+}
+
+int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+               int world_size, int64_t used_sequence, void* workspace, int64_t workspace_bytes,
+               float* mean_f32, void* mean_dtype, void* stream) {
+    const char* fn = "ulp_k_mean";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "k", k));
+    TRY(check_ptr(fn, "workspace", workspace));
+    TRY(check_ptr(fn, "mean_f32", mean_f32));
+    if (mean_dtype) TRY(check_ptr(fn, "mean_dtype", mean_dtype));
+    if (B > 65535 || B * H * D / 64 >= kMaxGrid ||
+        ulp::kmean_chunks(B, H, D, used_or_s(used_sequence, world_size * L)) > 65535)
+        return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
+    const int64_t need = ulp_k_mean_workspace_bytes(B, L, H, D, world_size, used_sequence);
+    if (workspace_bytes < need)
+        return fail(ULP_EINVAL, "%s: workspace of %lld bytes, %lld needed", fn,
+                    (long long)workspace_bytes, (long long)need);
+    ulp::KMeanLaunch a{};
+    a.k = static_cast<const uint16_t*>(k);
+    a.workspace = static_cast<double*>(workspace);
+    a.mean_f32 = mean_f32;
+    a.mean_dtype = static_cast<uint16_t*>(mean_dtype);
+    a.B = B; a.L = L; a.H = H; a.D = D;
+    a.used = used_or_s(used_sequence, world_size * L);
+    a.dtype = dtype;
+    return launched(ulp::launch_kmean(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

@@ -50,7 +50,21 @@ struct UnpackLaunch {
     int ndests;
 };
 
+struct KMeanLaunch {
+    const uint16_t* k;        // stacked shards [P, B, L, H, D]
+    double* workspace;        // [kmean_chunks(B, H, D, used), B, H*D] binary64
+    float* mean_f32;          // [B, H, D]
+    uint16_t* mean_dtype;     // [B, H, D] or nullptr
+    int64_t B, L, H, D, used;
+    int dtype;
+};
+
+// Rows per partial sum of the K mean, and the number of such chunks (workspace rows).
+int64_t kmean_rows(int64_t B, int64_t H, int64_t D, int64_t used);
+int64_t kmean_chunks(int64_t B, int64_t H, int64_t D, int64_t used);
+
 hipError_t launch_stats(const StatsLaunch& a, hipStream_t stream);
+hipError_t launch_kmean(const KMeanLaunch& a, hipStream_t stream);
 hipError_t launch_derive(const DeriveLaunch& a, hipStream_t stream);
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream);

@@ -134,3 +134,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ulp, "LIB_PATH", str(tmp_path / "libulp.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ulp.slots(100)
+
+
+def test_k_mean_validation(L):
+    # workspace size: 8 * B * H * D * ceil(used / R); small shapes take R = 32 rows
+    assert L.ulp_k_mean_workspace_bytes(2, 100, 4, 64, 2, NONE) == 8 * 2 * 4 * 64 * 7
+    assert L.ulp_k_mean_workspace_bytes(1, 1000, 4, 128, 4, NONE) == 8 * 4 * 128 * 125
+    assert L.ulp_k_mean_workspace_bytes(1, 1000, 4, 128, 4, 257) == 8 * 4 * 128 * 9
+    # a long sequence over many heads takes taller chunks, never more than 512 rows
+    big = L.ulp_k_mean_workspace_bytes(1, 9360, 40, 128, 8, 74000)
+    assert 8 * 40 * 128 * -(-74000 // 512) <= big <= 8 * 40 * 128 * -(-74000 // 32)
+    assert L.ulp_k_mean_workspace_bytes(1, 100, 4, 64, 2, 201) == 0
+    assert L.ulp_k_mean_workspace_bytes(0, 100, 4, 64, 2, NONE) == 0
+
+    need = L.ulp_k_mean_workspace_bytes(1, 128, 4, 64, 2, NONE)
+
+    def call(dtype=0, B=1, Lq=128, H=4, D=64, P=2, used=NONE, k=A, ws=A, wsb=need, mf=A,
+             md=A):
+        return L.ulp_k_mean(k, dtype, B, Lq, H, D, P, used, ws, wsb, mf, md, None)
+    assert call(wsb=need - 8) == EINVAL and b"workspace" in L.ulp_last_error()
+    assert call(used=257) == EINVAL and b"used_sequence" in L.ulp_last_error()
+    assert call(D=32) == EUNSUPPORTED
+    assert call(H=3) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(mf=A + 4) == EALIGN
+    assert call(md=A + 2) == EALIGN
+    assert call(ws=0) == EINVAL
+    assert call(B=70000, wsb=1 << 40) == EINVAL and b"too large" in L.ulp_last_error()

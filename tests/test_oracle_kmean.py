@@ -1,0 +1,78 @@
+"""Pins of the oracle's global K mean and of its dtype rounding (CPU only)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_attention_input_amd import workloads as W
+
+from helpers import small
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_dtype_rounding_matches_library(olib, dtype):
+    """binary32 -> bf16/fp16 round-to-nearest-even against torch's conversion: random
+    values over the whole range, exact ties, subnormals, overflow."""
+    rng = np.random.default_rng(0)
+    big = 3e38 if dtype == torch.bfloat16 else 7e4
+    vals = list((rng.standard_normal(20000) * 10.0 ** rng.integers(-8, 6, 20000)).astype(np.float32))
+    vals += list(rng.uniform(-big, big, 2000).astype(np.float32))
+    # exact midpoints between neighbouring values of the target format, and their neighbours
+    src = torch.randint(-30000, 30000, (3000,), generator=torch.Generator().manual_seed(1),
+                        dtype=torch.int32).to(torch.int16).view(dtype).float()
+    src = src[torch.isfinite(src)]
+    nxt = src.to(dtype).view(torch.int16).add(1).view(dtype).float()
+    ok = torch.isfinite(nxt)
+    mids = ((src[ok].double() + nxt[ok].double()) / 2).float()
+    for m in mids.tolist():
+        vals += [m, float(np.nextafter(np.float32(m), np.float32(np.inf))),
+                 float(np.nextafter(np.float32(m), np.float32(-np.inf)))]
+    vals += [0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 65504.0, 65519.0, 65520.0]
+    for v in vals:
+        v = float(np.float32(v))
+        if dtype == torch.float16 and abs(v) > 1e5:
+            continue
+        want = int(torch.tensor([v], dtype=torch.float32).to(dtype).view(torch.int16)) & 0xFFFF
+        assert oracle.dtype_bits(v, dtype) == want, (v, hex(want))
+
+
+def exact_mean_bits(ks, used, dtype):
+    """[P,B,L,H,D] -> the mean over rows [0, used) from the exactly rounded sum (math.fsum),
+    one correctly rounded binary64 division, then binary32 and the dtype (library rounding)."""
+    P, B, L, H, D = ks.shape
+    glob = ks.permute(1, 0, 2, 3, 4).reshape(B, P * L, H, D)[:, :used].double().numpy()
+    out = np.empty((B, H, D), np.float32)
+    for b in range(B):
+        for h in range(H):
+            for d in range(D):
+                out[b, h, d] = np.float32(math.fsum(glob[b, :, h, d].tolist()) / used)
+    t = torch.from_numpy(out)
+    return t, t.to(dtype)
+
+
+@pytest.mark.parametrize("shape", [(2, 1, 100, 2, 64), (4, 2, 33, 4, 64), (8, 1, 64, 8, 128)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_k_mean_against_exact_sum(olib, shape, dtype):
+    P, B, L, H, D = shape
+    rng = torch.Generator().manual_seed(sum(shape))
+    mu = torch.randn(H, D, generator=rng) * 8
+    ks = (mu + 0.1 * torch.randn(P, B, L, H, D, generator=rng)).to(dtype)
+    for used in (P * L, P * L - 7, 1, 65):
+        used = max(1, min(used, P * L))
+        mf, md = oracle.k_mean(ks, used_sequence=used)
+        ef, ed = exact_mean_bits(ks, used, dtype)
+        assert torch.equal(mf.view(torch.int32), ef.view(torch.int32))
+        assert torch.equal(md.view(torch.int16), ed.view(torch.int16))
+
+
+def test_k_mean_matches_workload_recipe(olib):
+    """The workloads' k_mean_global (chunked float64 sum) is the same definition."""
+    for w in (small(P=4, L=100, H=4, D=64, used=333, seed=3),
+              small(P=2, L=300, H=2, D=128, dtype=torch.float16, seed=4)):
+        d = W.generate(w)
+        _, md = oracle.k_mean(W.stacked_shards(d["K"], w.P), used_sequence=w.used)
+        assert torch.equal(md.view(torch.int16), d["mean"].view(torch.int16))
