@@ -63,7 +63,8 @@ def _load(path: str = LIB_PATH):
     lib.ora_boundary_minmax.restype = None
     lib.ora_derive_k_boundary_amax.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, i64]
     lib.ora_derive_k_boundary_amax.restype = None
-    lib.ora_pack.argtypes = [vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i64, i64, vp, i64]
+    lib.ora_pack.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp,
+                             i64]
     lib.ora_pack.restype = None
     lib.ora_unpack_for_sage.argtypes = [vp, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.ora_unpack_for_sage.restype = None
@@ -150,15 +151,20 @@ def derive_k_boundary_amax(grouped, gathered, mean, *, rank, local_sequence, wor
     return grouped
 
 
-def pack(q, k, v, mean, q_amax, k_amax, *, rank, world_size, _lib=None):
-    """-> send buffer [world_size, chunk_bytes] uint8 (chunk p for destination p)."""
+def pack(q, k, v, mean, q_amax, k_amax, *, rank, world_size, v_scale=None, _lib=None):
+    """-> send buffer [world_size, chunk_bytes] uint8 (chunk p for destination p).
+    v_scale: optional [B,H,D] float32 divisor of V before E4M3."""
     lb = _lib or lib()
     B, L, H, D = q.shape
     h = H // world_size
     cb = chunk_bytes(B, L, h, D)
     send = torch.empty(world_size, cb, dtype=torch.uint8)
+    if v_scale is not None:
+        v_scale = v_scale.to(torch.float32).contiguous()
+        assert v_scale.shape == (B, H, D)
     lb.ora_pack(_p(q), _p(k), _p(v), _p(mean), _dt(q), _p(q_amax.contiguous()),
-                _p(k_amax.contiguous()), B, L, H, D, rank, world_size, _p(send), cb)
+                _p(k_amax.contiguous()), _p(v_scale), B, L, H, D, rank, world_size, _p(send),
+                cb)
     return send
 
 

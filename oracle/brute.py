@@ -67,8 +67,9 @@ def e4m3_bytes(v: torch.Tensor) -> torch.Tensor:
     return v.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def define(Q, K, V, mean, *, world_size, used_sequence=None):
-    """Q, K, V: global [B,S,H,D] bf16/fp16; mean: [B,H,D] same dtype.
+def define(Q, K, V, mean, *, world_size, used_sequence=None, v_scale=None):
+    """Q, K, V: global [B,S,H,D] bf16/fp16; mean: [B,H,D] same dtype; v_scale: optional
+    [B,H,D] float32 divisor of V (the caller's V scale, unpack_for_sage Returns).
 
     Returns a dict with, for the live groups g < ceil(used/64):
       q_amax, k_amax   [B,H,G] fp32
@@ -91,7 +92,8 @@ def define(Q, K, V, mean, *, world_size, used_sequence=None):
         G=G, rows=rows, used=used,
         q_amax=q_amax, k_amax=k_amax, q_scale=q_scale, k_scale=k_scale,
         q8=quantize_rows(xq, q_scale, rows), k8=quantize_rows(xk, k_scale, rows),
-        v8=e4m3_bytes(V.float()),
+        v8=e4m3_bytes(V.float() if v_scale is None
+                      else rn32_div(V.float(), v_scale.float()[:, None].expand_as(V))),
     )
     h = H // world_size
 

@@ -39,7 +39,9 @@
  *     rank's first (0) or last (1) touched group, dim 3 picks min (0) or max (1).
  *   - Q uses the same machinery with the mean taken as +0 (raw values).
  *   - scale = amax/127; q = clamp(rint(x/scale), -127, 127) with x/scale the IEEE quotient.
- *   - V is converted unscaled to OCP E4M3FN, round-to-nearest-even, saturating at 448.
+ *   - V is converted to OCP E4M3FN, round-to-nearest-even, saturating at 448; unscaled by
+ *     default, or divided first (one IEEE binary32 division) by the caller's V scale
+ *     [B,H,D] when one is given (unpack_for_sage Returns: the V scale stays with the caller).
  *   - Chunk (source r -> destination p): sections q8, k8, v8 each [B,L,h,D] bytes for
  *     heads p*h..p*h+h-1, then q_scale and k_scale each [B,h,slots] fp32; every section
  *     starts on a 256-byte boundary and padding bytes are 0.
@@ -239,10 +241,12 @@ void ora_derive_k_boundary_amax(float* grouped, const float* gathered, const uin
 /* ------------------------------------------------------------------ step 4: pack */
 
 /* Quantize this rank's shard and write one chunk per destination p at send + p*stride.
- * q_amax, k_amax: [B,H,slots(L)] after derive.  mean: [B,H,D] (K is centered by it). */
+ * q_amax, k_amax: [B,H,slots(L)] after derive.  mean: [B,H,D] (K is centered by it).
+ * v_scale: [B,H,D] binary32 divisor of V before the E4M3 conversion, or NULL (unscaled). */
 void ora_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* mean,
-              int dtype, const float* q_amax, const float* k_amax, int64_t B, int64_t L,
-              int64_t H, int64_t D, int64_t rank, int64_t P, uint8_t* send, int64_t stride) {
+              int dtype, const float* q_amax, const float* k_amax, const float* v_scale,
+              int64_t B, int64_t L, int64_t H, int64_t D, int64_t rank, int64_t P,
+              uint8_t* send, int64_t stride) {
     int64_t h = H / P;
     int64_t slots = ora_slots(L);
     int64_t sec = align256(B * L * h * D);
@@ -273,7 +277,9 @@ void ora_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uin
                         float kc = elem(k, src, dtype) - elem(mean, (b * H + hh) * D + d, dtype);
                         q8[dst] = ora_quant_i8(elem(q, src, dtype), sq);
                         k8[dst] = ora_quant_i8(kc, sk);
-                        v8[dst] = ora_e4m3(elem(v, src, dtype));
+                        float vf = elem(v, src, dtype);
+                        if (v_scale) vf = vf / v_scale[(b * H + hh) * D + d];
+                        v8[dst] = ora_e4m3(vf);
                     }
                 }
             }

@@ -22,11 +22,12 @@ def shards(X: torch.Tensor, world_size: int):
 
 
 def run_group(Q, K, V, mean, *, world_size, used_sequence=None, scale_sequence=None,
-              destinations=None, _lib=None):
+              destinations=None, v_scale=None, _lib=None):
     """Q, K, V: global [B,S,H,D]; mean [B,H,D].  Returns every intermediate:
     q_minmax/k_minmax [P,B,H,2,2,D], q_amax_kernel/k_amax_kernel (before derive) and
     q_amax/k_amax (after derive) per rank, send buffers per rank, and the unpack 5-tuple
-    per destination (all destinations unless ``destinations`` lists a subset)."""
+    per destination (all destinations unless ``destinations`` lists a subset).  v_scale:
+    the caller's optional [B,H,D] V divisor."""
     P = world_size
     B, S, H, D = Q.shape
     L = S // P
@@ -46,7 +47,8 @@ def run_group(Q, K, V, mean, *, world_size, used_sequence=None, scale_sequence=N
         derive_k_boundary_amax(q_amax[r], q_mm, None, rank=r, local_sequence=L,
                                dtype=Q.dtype, **kw)
         derive_k_boundary_amax(k_amax[r], k_mm, mean, rank=r, local_sequence=L, **kw)
-    sends = [pack(qs[r], ks[r], vs[r], mean, q_amax[r], k_amax[r], rank=r, **kw)
+    sends = [pack(qs[r], ks[r], vs[r], mean, q_amax[r], k_amax[r], rank=r, v_scale=v_scale,
+                  **kw)
              for r in range(P)]
     dests = range(P) if destinations is None else destinations
     outs = {}

@@ -139,3 +139,13 @@ def sample_heads(w: Workload, per_dest: int = 1, seed: int = 12345) -> list[int]
         pick = torch.randperm(w.h, generator=g)[:per_dest].sort().values
         heads += [p * w.h + int(j) for j in pick]
     return heads
+
+
+def v_scale(w: Workload, seed: int | None = None) -> torch.Tensor:
+    """A caller-held V scale [B,H,D] float32 (the pages leave its origin to the caller):
+    2^u with u uniform in [-7, 2) drawn in float32 by a generator seeded with the workload's
+    seed + 1000, so that mantissas are arbitrary and V / scale spans E4M3's subnormals,
+    normals and saturation."""
+    g = torch.Generator().manual_seed(w.seed + 1000 if seed is None else seed)
+    u = torch.empty(w.B, w.H, w.D).uniform_(-7.0, 2.0, generator=g)
+    return torch.exp2(u).contiguous()

@@ -18,6 +18,7 @@ import torch
 import oracle
 import test_oracle_pins as pins
 import test_oracle_pipeline as pipe
+import test_oracle_vscale as vsc
 from helpers import small
 
 MUTANTS = {
@@ -54,6 +55,11 @@ MUTANTS = {
     "unpack_v_transpose": ("v8[((b * D + d) * h + j) * spad + t] = vb;",
                            "v8[((b * h + j) * D + d) * spad + t] = vb;"),
     "slots_formula": ("(L + ORA_GROUP - 1) / ORA_GROUP + 1", "(L + ORA_GROUP - 1) / ORA_GROUP"),
+    "v_scale_multiplies": ("vf = vf / v_scale[(b * H + hh) * D + d];",
+                           "vf = vf * v_scale[(b * H + hh) * D + d];"),
+    "v_scale_local_head": ("vf = vf / v_scale[(b * H + hh) * D + d];",
+                           "vf = vf / v_scale[(b * H + j) * D + d];"),
+    "v_scale_ignored": ("if (v_scale) vf = vf / v_scale[(b * H + hh) * D + d];", ""),
 }
 
 
@@ -69,6 +75,8 @@ def battery():
         ("worked_example", lambda: pipe.test_hand_worked_example(None)),
         ("padding_only", lambda: pipe.test_padding_only_slice_contributes_floor(None)),
         ("only_partial_live", lambda: pipe.test_only_partial_live_group_changes(None, 195)),
+        ("v_scale_hand", lambda: vsc.test_hand_worked_values(None)),
+        ("v_scale_definition", lambda: vsc.test_v_scale_matches_definition(None, vsc.CASES[0])),
     ]
     for w in [small(B=2, P=4, L=100, H=8, D=64, used=301, scale_sequence=301, seed=1),
               small(P=2, L=65, H=4, D=128, dtype=torch.float16, used=100, seed=2),
