@@ -30,7 +30,7 @@ KERNEL_SOURCES = ["precision_attention_input_amd/csrc/pack.hip",
                   "precision_attention_input_amd/csrc/ulp_device.h"]
 
 
-def algorithmic_bytes(w) -> dict:
+def algorithmic_bytes(w, v_scale: bool = False) -> dict:
     """Bytes the method must move (read + write), per step, by kernel.
     N = B*S*H*D elements per tensor, e = 2 bytes, sigma = slots(L), W = scale width."""
     import precision_attention_input_amd as ulp
@@ -42,6 +42,8 @@ def algorithmic_bytes(w) -> dict:
     Wd = ulp.scale_widths(w.scale_sequence or S)[0]
     spad = (S + 63) // 64 * 64
     pack = 3 * e * N + 8 * B * H * sigma * P + P * e * B * H * D + 3 * N + 8 * B * H * sigma * P
+    if v_scale:
+        pack += P * 4 * B * H * D          # every rank reads the caller's [B,H,D] V scale
     unpack = 3 * N + 8 * B * H * Wd + 2 * N + B * D * H * spad + 8 * B * H * Wd
     # fused statistics: read Q and K once, the mean per rank; write both amax tensors and
     # both boundary min/max tensors
@@ -151,6 +153,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--v-scale", action="store_true",
+                    help="pass a caller-held [B,H,D] V scale to the pack (V divided before "
+                         "E4M3); the default converts V unscaled")
     ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
                     help="kernel FETCH_SIZE csv, kernel WRITE_SIZE csv, copy FETCH_SIZE csv, "
                          "copy WRITE_SIZE csv (rocprofv3 --pmc counter_collection files of this "
@@ -190,7 +195,8 @@ def main():
 
     w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
     d = W.generate(w)
-    nb = algorithmic_bytes(w)
+    nb = algorithmic_bytes(w, args.v_scale)
+    vsc = W.v_scale(w).to(dev) if args.v_scale else None
     set_bytes = 12 * nb["N"]      # stacked Q/K/V (6N) + all-to-all buffer (3N) + outputs (3N)
     nsets = args.sets or max(2, min(8, -(-1024 * 2 ** 20 // set_bytes)))
     P, L, B, H, D = w.P, w.L, w.B, w.H, w.D
@@ -219,7 +225,7 @@ def main():
         if ev:
             ev[2].record()
         ulp.group_pack(s["Q"], s["K"], s["V"], s["mean"], qa, ka, world_size=P,
-                       group=s["group"])
+                       v_scale=vsc, group=s["group"])
         if ev:
             ev[3].record()
         ulp.group_unpack(s["group"], batch_size=B, local_sequence=L, local_heads=w.h,
@@ -267,7 +273,7 @@ def main():
     pu_bytes = nb["pack"] + nb["unpack"]
     value = pu_bytes / ((pack_ms + unpack_ms) * 1e-3) / 1e9
     pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
-    traffic = load_traffic(w.name, nb["pack"])
+    traffic = None if args.v_scale else load_traffic(w.name, nb["pack"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -294,7 +300,7 @@ def main():
         "config": {"workload": w.name, "B": B, "world_size": P, "local_sequence": L,
                    "heads": H, "head_dim": D, "used_sequence": w.used,
                    "scale_sequence": w.scale_sequence, "aligned": w.aligned,
-                   "buffer_sets": nsets},
+                   "v_scale": bool(args.v_scale), "buffer_sets": nsets},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "pack_unpack_bytes": pu_bytes,
         "pack_ms": round(pack_ms, 5),

@@ -125,17 +125,22 @@ int ulp_derive_k_boundary_amax(float* grouped_amax, const float* gathered_minmax
  * Per slot: scale = RN(amax / 127).  Per element of row l (slot of global row r*L + l):
  *   q8 = clamp(rint(RN(fp32(q) / q_scale)), -127, 127)
  *   k8 = clamp(rint(RN(RN(fp32(k) - fp32(k_mean)) / k_scale)), -127, 127)
- *   v8 = E4M3FN(fp32(v)), round to nearest even, saturating to +-448.
+ *   v8 = E4M3FN(fp32(v)), round to nearest even, saturating to +-448; with a V scale,
+ *        E4M3FN(RN(fp32(v) / v_scale[b, head, d])) (one IEEE binary32 division).
  *   q, k, v         [B, L, H, D] dtype.
  *   k_mean          [B, H, D] dtype.
  *   q_amax, k_amax  [B, H, slots(L)] float (after derive).
+ *   v_scale         NULL (V unscaled), or [B, H, D] float indexed by global head: the V
+ *                   scale that unpack_for_sage's Returns leave with the caller, which passes
+ *                   it on to the consumer itself.  Values should be positive and finite;
+ *                   others give whatever the IEEE quotient gives (0 -> +-448, NaN -> NaN).
  *   send            chunk for destination p at send + p * dest_stride_bytes; each chunk is
  *                   ulp_chunk_bytes(B, L, H/P, D) bytes.  dest_stride_bytes must be a
  *                   multiple of 256 and >= the chunk size. */
 int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
-             const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
-             int64_t D, int rank, int world_size, uint8_t* send, int64_t dest_stride_bytes,
-             void* stream);
+             const float* q_amax, const float* k_amax, const float* v_scale, int64_t B,
+             int64_t L, int64_t H, int64_t D, int rank, int world_size, uint8_t* send,
+             int64_t dest_stride_bytes, void* stream);
 
 /* unpack_for_sage (flashinfer.comm._ulysses_lowp.unpack_for_sage: description, Returns).
  * Turns the P received chunks into contiguous logical Q/K, transposed V with a zero global
@@ -174,10 +179,12 @@ int ulp_group_derive(float* q_amax, float* k_amax, const float* q_minmax,
                      int64_t H, int64_t D, int64_t local_sequence, int world_size,
                      void* stream);
 
-/* ulp_pack for every rank into the all-to-all buffer `group` (layout above). */
+/* ulp_pack for every rank into the all-to-all buffer `group` (layout above); v_scale
+ * [B, H, D] (or NULL) is shared by every rank. */
 int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
-                   const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
-                   int64_t D, int world_size, uint8_t* group, void* stream);
+                   const float* q_amax, const float* k_amax, const float* v_scale, int64_t B,
+                   int64_t L, int64_t H, int64_t D, int world_size, uint8_t* group,
+                   void* stream);
 
 /* ulp_unpack_for_sage for every destination; outputs are stacked over destinations:
  * q8, k8 [P, B, S, h, D]; v8 [P, B, D, h, Spad]; q_scale, k_scale [P, B, h, W]. */

@@ -57,15 +57,15 @@ def lib():
             "ulp_boundary_minmax": ([vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
             "ulp_derive_k_boundary_amax": ([vp, vp, vp, i32, i64, i64, i64, i32, i64, i32, vp],
                                            i32),
-            "ulp_pack": ([vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64, vp],
-                         i32),
+            "ulp_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64,
+                          vp], i32),
             "ulp_unpack_for_sage": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp,
                                      vp], i32),
             "ulp_group_stats": ([vp, vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, vp, vp, vp,
                                  vp], i32),
             "ulp_group_derive": ([vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp], i32),
-            "ulp_group_pack": ([vp, vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, vp, vp],
-                               i32),
+            "ulp_group_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, vp,
+                                vp], i32),
             "ulp_group_unpack": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp],
                                  i32),
             "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
@@ -176,18 +176,27 @@ def derive_k_boundary_amax(grouped_amax, gathered_minmax, k_mean_global, *, rank
     return grouped_amax
 
 
-def pack(q, k, v, k_mean_global, q_amax, k_amax, *, rank, world_size, send=None,
+def _v_scale(v_scale, B, H, D):
+    if v_scale is not None and (v_scale.dtype != torch.float32 or
+                                tuple(v_scale.shape) != (B, H, D)):
+        raise ValueError(f"v_scale must be float32 [{B}, {H}, {D}], got {v_scale.dtype} "
+                         f"{tuple(v_scale.shape)}")
+
+
+def pack(q, k, v, k_mean_global, q_amax, k_amax, *, rank, world_size, v_scale=None, send=None,
          dest_stride=None):
     """Quantize one rank's shard; returns the send buffer [world_size, chunk_bytes] uint8
-    (or writes chunk p at ``send`` + p * dest_stride bytes when ``send`` is given)."""
-    _dev(q, k, v, k_mean_global, q_amax, k_amax)
+    (or writes chunk p at ``send`` + p * dest_stride bytes when ``send`` is given).
+    v_scale: the caller's optional [B,H,D] float32 V divisor, applied before E4M3."""
+    _dev(q, k, v, k_mean_global, q_amax, k_amax, v_scale)
     B, L, H, D = q.shape
+    _v_scale(v_scale, B, H, D)
     cb = chunk_bytes(B, L, H // world_size, D)
     if send is None:
         send = torch.empty(world_size, cb, dtype=torch.uint8, device=q.device)
         dest_stride = cb
     _check(lib().ulp_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
-                          _p(k_amax), B, L, H, D, rank, world_size, _p(send),
+                          _p(k_amax), _p(v_scale), B, L, H, D, rank, world_size, _p(send),
                           dest_stride or cb, _stream(q)))
     return send
 
@@ -253,14 +262,17 @@ def group_buffer(batch_size, local_sequence, heads, head_dim, world_size, device
     return torch.empty(world_size, world_size, cb, dtype=torch.uint8, device=device)
 
 
-def group_pack(q, k, v, k_mean_global, q_amax, k_amax, *, world_size, group=None):
+def group_pack(q, k, v, k_mean_global, q_amax, k_amax, *, world_size, v_scale=None,
+               group=None):
     """Every rank's pack into the all-to-all buffer [P_dst, P_src, chunk_bytes]."""
     P, B, L, H, D = q.shape
     if group is None:
         group = group_buffer(B, L, H, D, world_size, q.device)
-    _dev(q, k, v, k_mean_global, q_amax, k_amax, group)
+    _dev(q, k, v, k_mean_global, q_amax, k_amax, v_scale, group)
+    _v_scale(v_scale, B, H, D)
     _check(lib().ulp_group_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
-                                _p(k_amax), B, L, H, D, world_size, _p(group), _stream(q)))
+                                _p(k_amax), _p(v_scale), B, L, H, D, world_size, _p(group),
+                                _stream(q)))
     return group
 
 

@@ -178,9 +178,9 @@ int ulp_derive_k_boundary_amax(float* grouped_amax, const float* gathered_minmax
 }
 
 int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
-             const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
-             int64_t D, int rank, int world_size, uint8_t* send, int64_t dest_stride_bytes,
-             void* stream) {
+             const float* q_amax, const float* k_amax, const float* v_scale, int64_t B,
+             int64_t L, int64_t H, int64_t D, int rank, int world_size, uint8_t* send,
+             int64_t dest_stride_bytes, void* stream) {
     const char* fn = "ulp_pack";
     TRY(check_shape(fn, dtype, B, L, H, D, world_size, rank, true));
     TRY(check_ptr(fn, "q", q));
@@ -189,6 +189,7 @@ int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, in
     TRY(check_ptr(fn, "k_mean", k_mean));
     TRY(check_ptr(fn, "q_amax", q_amax));
     TRY(check_ptr(fn, "k_amax", k_amax));
+    if (v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
     TRY(check_ptr(fn, "send", send));
     const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
     if (dest_stride_bytes % 256 != 0)
@@ -204,6 +205,7 @@ int ulp_pack(const void* q, const void* k, const void* v, const void* k_mean, in
     a.mean = static_cast<const uint16_t*>(k_mean);
     a.q_amax = q_amax;
     a.k_amax = k_amax;
+    a.v_scale = v_scale;
     a.send = send;
     a.dest_stride = dest_stride_bytes;
     a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
@@ -309,8 +311,9 @@ int ulp_group_derive(float* q_amax, float* k_amax, const float* q_minmax,
 }
 
 int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
-                   const float* q_amax, const float* k_amax, int64_t B, int64_t L, int64_t H,
-                   int64_t D, int world_size, uint8_t* group, void* stream) {
+                   const float* q_amax, const float* k_amax, const float* v_scale, int64_t B,
+                   int64_t L, int64_t H, int64_t D, int world_size, uint8_t* group,
+                   void* stream) {
     const char* fn = "ulp_group_pack";
     TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
     TRY(check_ptr(fn, "q", q));
@@ -319,6 +322,7 @@ int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_me
     TRY(check_ptr(fn, "k_mean", k_mean));
     TRY(check_ptr(fn, "q_amax", q_amax));
     TRY(check_ptr(fn, "k_amax", k_amax));
+    if (v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
     TRY(check_ptr(fn, "group", group));
     const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
     ulp::PackLaunch a{};
@@ -328,6 +332,7 @@ int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_me
     a.mean = static_cast<const uint16_t*>(k_mean);
     a.q_amax = q_amax;
     a.k_amax = k_amax;
+    a.v_scale = v_scale;
     a.send = group;
     a.dest_stride = (int64_t)world_size * cb;
     a.x_rank_stride = B * L * H * D;

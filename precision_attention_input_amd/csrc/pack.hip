@@ -4,7 +4,8 @@
 // scale = RN(amax / 127); every element becomes
 //   q8 = clamp(rint(RN(fp32(q) / q_scale)), -127, 127)
 //   k8 = clamp(rint(RN(RN(fp32(k) - fp32(mean)) / k_scale)), -127, 127)
-//   v8 = E4M3FN(fp32(v)) (nearest even, saturating)
+//   v8 = E4M3FN(fp32(v)) (nearest even, saturating), or E4M3FN(RN(fp32(v) / v_scale)) with
+//        the caller's [B, H, D] V scale (unpack_for_sage Returns: it stays with the caller)
 // and lands in the chunk of the destination owning its head (unpack_for_sage Parameters:
 // local_heads = H / world_size, contiguous per destination).  Chunk sections: q8, k8, v8
 // [B, L, h, D] bytes, then q_scale, k_scale [B, h, slots] fp32, each 256-byte aligned.
@@ -29,7 +30,7 @@ constexpr int kRows = kThreads / kCols;   // rows per workgroup
 
 struct PackParams {
     const uint16_t *q, *k, *v, *mean;
-    const float *q_amax, *k_amax;
+    const float *q_amax, *k_amax, *v_scale;
     uint8_t* send;
     int64_t dest_stride, x_rank_stride, amax_rank_stride, send_rank_stride;
     int64_t B, L, H, h, P, slots, sec, ssec;
@@ -91,7 +92,25 @@ __device__ __forceinline__ uint4 e4m3x16(const uint4& x0, const uint4& x1) {
                       e4m3x4(f[8], f[9], f[10], f[11]), e4m3x4(f[12], f[13], f[14], f[15]));
 }
 
-template <int DT, int D, bool NT>
+// V divided by the caller's scale (one correctly rounded binary32 division per value: the
+// compiler's default single-precision division on gfx950), then E4M3.
+template <int DT>
+__device__ __forceinline__ uint4 e4m3x16_scaled(const uint4& x0, const uint4& x1,
+                                                const float4* sv) {
+    float f[16];
+    decode16<DT>(x0, x1, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[4 * i] = f[4 * i] / sv[i].x;
+        f[4 * i + 1] = f[4 * i + 1] / sv[i].y;
+        f[4 * i + 2] = f[4 * i + 2] / sv[i].z;
+        f[4 * i + 3] = f[4 * i + 3] / sv[i].w;
+    }
+    return make_uint4(e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7]),
+                      e4m3x4(f[8], f[9], f[10], f[11]), e4m3x4(f[12], f[13], f[14], f[15]));
+}
+
+template <int DT, int D, bool NT, bool VS>
 __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     constexpr int VPH = D / 16;      // 16-element vectors per head row
     const int64_t L = p.L, H = p.H, h = p.h;
@@ -139,6 +158,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     const uint4 v1 = load16(p.v + xo + 8);
     const uint16_t* mp = p.mean + ((uint64_t)b * H + head) * D + dv * 16;
     const uint4 m0 = load16(mp), m1 = load16(mp + 8);
+    float4 sv[4];
+    if constexpr (VS) {
+        const float4* vp = reinterpret_cast<const float4*>(
+            p.v_scale + ((uint64_t)b * H + head) * D + dv * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[i] = vp[i];
+    }
     // Keep every load above this point: each wave then has all of its reads in flight at
     // once instead of one tensor's at a time.
     __builtin_amdgcn_sched_barrier(0);
@@ -150,7 +176,10 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
 
     store16<NT>(out, quantize16<DT, false, DT == kBF16>(q0, q1, m0, m1, sq));
     store16<NT>(out + p.sec, quantize16<DT, true, true>(k0, k1, m0, m1, sk));
-    store16<NT>(out + 2 * p.sec, e4m3x16<DT>(v0, v1));
+    if constexpr (VS)
+        store16<NT>(out + 2 * p.sec, e4m3x16_scaled<DT>(v0, v1, sv));
+    else
+        store16<NT>(out + 2 * p.sec, e4m3x16<DT>(v0, v1));
 
     if (dv == 0) {
         // The first row of each touched group writes its scales; row 0 also writes the
@@ -181,6 +210,7 @@ hipError_t launch_t(const PackLaunch& a, hipStream_t stream) {
     p.mean = a.mean;
     p.q_amax = a.q_amax;
     p.k_amax = a.k_amax;
+    p.v_scale = a.v_scale;
     p.send = a.send;
     p.dest_stride = a.dest_stride;
     p.x_rank_stride = a.x_rank_stride;
@@ -202,10 +232,15 @@ hipError_t launch_t(const PackLaunch& a, hipStream_t stream) {
     const int64_t col_blocks = (a.H * (a.D / 16) + kCols - 1) / kCols;
     dim3 grid((unsigned)(a.B * p.row_blocks), (unsigned)col_blocks, (unsigned)a.nranks);
     const int64_t written = a.nranks * 3 * a.B * a.L * a.H * a.D;   // code bytes of this launch
-    if (written > kResidentBytes)
-        hipLaunchKernelGGL((pack_kernel<DT, D, true>), grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((pack_kernel<DT, D, false>), grid, dim3(kThreads), 0, stream, p);
+    const bool nt = written > kResidentBytes;
+    const dim3 block(kThreads);
+    if (a.v_scale) {
+        if (nt) hipLaunchKernelGGL((pack_kernel<DT, D, true, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((pack_kernel<DT, D, false, true>), grid, block, 0, stream, p);
+    } else {
+        if (nt) hipLaunchKernelGGL((pack_kernel<DT, D, true, false>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((pack_kernel<DT, D, false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct DeriveLaunch {
 struct PackLaunch {
     const uint16_t *q, *k, *v, *mean;   // shards of rank rank0 [B, L, H, D]; mean [B, H, D]
     const float *q_amax, *k_amax;       // [B, H, slots] of rank rank0
+    const float* v_scale;               // [B, H, D] V divisor (shared by all ranks) or nullptr
     uint8_t* send;                      // chunk (rank0 -> p) at send + p * dest_stride
     int64_t dest_stride;
     int64_t x_rank_stride, amax_rank_stride, send_rank_stride;

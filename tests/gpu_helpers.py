@@ -44,8 +44,9 @@ def to_dev(d: dict, P: int) -> dict:
     return out
 
 
-def run_per_rank(w: W.Workload, dd: dict, aligned=None) -> dict:
-    """Every rank through the per-rank entry points; the all-to-all is the [P,P,cb] buffer."""
+def run_per_rank(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
+    """Every rank through the per-rank entry points; the all-to-all is the [P,P,cb] buffer.
+    v_scale: optional [B,H,D] float32 device tensor (the caller's V divisor)."""
     P, L = w.P, w.L
     kw = dict(world_size=P, used_sequence=w.used)
     qs = [dd["Q"][r] for r in range(P)]
@@ -65,7 +66,7 @@ def run_per_rank(w: W.Workload, dd: dict, aligned=None) -> dict:
     cb = grp.shape[-1]
     for r in range(P):
         ulp.pack(qs[r], ks[r], vs[r], dd["mean"], qa[r], ka[r], rank=r, world_size=P,
-                 send=grp[0, r], dest_stride=P * cb)
+                 v_scale=v_scale, send=grp[0, r], dest_stride=P * cb)
     outs = {}
     for p in range(P):
         outs[p] = ulp.unpack_for_sage(grp[p], batch_size=w.B, local_sequence=L,
@@ -77,14 +78,15 @@ def run_per_rank(w: W.Workload, dd: dict, aligned=None) -> dict:
                 sends=[grp[:, r] for r in range(P)], outs=outs)
 
 
-def run_group(w: W.Workload, dd: dict, aligned=None) -> dict:
+def run_group(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     """The whole group through the group entry points (the benchmark's launch sequence)."""
     P, L = w.P, w.L
     qa, ka, qm, km = ulp.group_stats(dd["Q"], dd["K"], dd["mean"], world_size=P,
                                      used_sequence=w.used)
     qa_kernel, ka_kernel = qa.clone(), ka.clone()
     ulp.group_derive(qa, ka, qm, km, dd["mean"], local_sequence=L, world_size=P)
-    grp = ulp.group_pack(dd["Q"], dd["K"], dd["V"], dd["mean"], qa, ka, world_size=P)
+    grp = ulp.group_pack(dd["Q"], dd["K"], dd["V"], dd["mean"], qa, ka, world_size=P,
+                         v_scale=v_scale)
     o = ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
                          world_size=P, aligned=aligned, scale_sequence=w.scale_sequence)
     torch.cuda.synchronize()

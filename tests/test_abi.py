@@ -98,7 +98,7 @@ def test_minmax_and_derive_validation(L):
 
 def test_pack_validation(L):
     cb = ulp.chunk_bytes(1, 128, 2, 64)
-    args = [A, A, A, A, 0, A, A, 1, 128, 4, 64, 0, 2, A]
+    args = [A, A, A, A, 0, A, A, None, 1, 128, 4, 64, 0, 2, A]
     assert L.ulp_pack(*args, cb + 16, None) == EALIGN
     assert b"multiple of 256" in L.ulp_last_error()
     assert L.ulp_pack(*args, cb - 256, None) == EINVAL
@@ -106,6 +106,9 @@ def test_pack_validation(L):
     bad = list(args)
     bad[3] = 0                      # k_mean is required by pack
     assert L.ulp_pack(*bad, cb, None) == EINVAL
+    bad = list(args)
+    bad[7] = A + 4                  # an optional V scale must be aligned like every tensor
+    assert L.ulp_pack(*bad, cb, None) == EALIGN and b"v_scale" in L.ulp_last_error()
 
 
 def test_unpack_validation(L):
@@ -124,7 +127,8 @@ def test_unpack_validation(L):
 def test_group_validation(L):
     assert L.ulp_group_stats(A, A, 0, 0, 1, 128, 4, 64, 2, NONE, A, A, A, A, None) == EINVAL
     assert L.ulp_group_derive(A, A, A, A, A, 0, 1, 4, 64, 128, 3, None) == EUNSUPPORTED
-    assert L.ulp_group_pack(A, A, A, A, 0, A, A, 1, 128, 3, 64, 2, A, None) == EINVAL
+    assert L.ulp_group_pack(A, A, A, A, 0, A, A, None, 1, 128, 3, 64, 2, A, None) == EINVAL
+    assert L.ulp_group_pack(A, A, A, A, 0, A, A, A + 8, 1, 128, 4, 64, 2, A, None) == EALIGN
     assert L.ulp_group_unpack(A, 1, 100, 2, 64, 2, 1, NONE, A, A, A, A, A, None) == EINVAL
 
 
