@@ -1,0 +1,69 @@
+"""A consumer of the unpacked tensors: attention over INT8 Q/K and FP8 E4M3 V, in float64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The unpack_for_sage page names the consumer (the Sage attention kernel) and the layouts
+it is handed: q8, k8 INT8 [B, S, h, D] with one FP32 scale per 64-row group in
+q_scale, k_scale [B, h, W]; v8 FP8 E4M3 [B, D, h, ceil(S/64)*64]; the V scale stays with
+the caller.  This module reads them the way such a consumer would -- a score is the
+integer dot product of a Q row and a K row times the two rows' group scales, the softmax
+runs over the live keys only, and the output weights the decoded E4M3 values (times the
+caller's V scale, if any) -- but in float64 and without tiling, so that the result
+depends only on the stored bytes and their layouts.  Smooth K needs no correction: a
+per-channel mean removed from every key shifts every score of a query row by the same
+amount, which the softmax cancels.
+
+``reference_attention`` is the same attention on the original bf16/fp16 Q, K, V.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+GROUP = 64
+
+
+def e4m3_values(v8: torch.Tensor) -> torch.Tensor:
+    """E4M3FN bytes -> float64 values (library decode)."""
+    return v8.contiguous().view(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def quantized_attention(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries, used: int,
+                        v_scale_row=None) -> torch.Tensor:
+    """Output rows [len(queries), D] of local head j of batch entry b, from one
+    destination's unpacked tensors (CPU).  Keys t < used; v_scale_row: optional [D]."""
+    qi = torch.as_tensor(queries, dtype=torch.int64)
+    D = q8.shape[-1]
+    q = q8[b, qi, j].to(torch.float64)                       # [nq, D] integers
+    k = k8[b, :used, j].to(torch.float64)                    # [nk, D]
+    dots = q @ k.T                                           # exact: |sum| < 2^21
+    keys = torch.arange(used)
+    scores = dots * q_scale[b, j, qi // GROUP].double()[:, None] \
+        * k_scale[b, j, keys // GROUP].double()[None, :]
+    p = torch.softmax(scores / math.sqrt(D), dim=-1)
+    v = e4m3_values(v8[b, :, j, :used]).T                    # [nk, D]
+    if v_scale_row is not None:
+        v = v * v_scale_row.double()[None, :]
+    return p @ v
+
+
+def reference_attention(Q, K, V, *, b: int, head: int, queries, used: int) -> torch.Tensor:
+    """The same rows from the original global Q, K, V [B, S, H, D] (bf16/fp16 values) in
+    float64."""
+    qi = torch.as_tensor(queries, dtype=torch.int64)
+    D = Q.shape[-1]
+    q = Q[b, qi, head].double()
+    k = K[b, :used, head].double()
+    v = V[b, :used, head].double()
+    p = torch.softmax((q @ k.T) / math.sqrt(D), dim=-1)
+    return p @ v
+
+
+def compare(out: torch.Tensor, ref: torch.Tensor) -> dict:
+    """Cosine similarity and relative L2 / max errors of out against ref."""
+    o, r = out.flatten().double(), ref.flatten().double()
+    cos = float((o @ r) / (o.norm() * r.norm()).clamp_min(1e-300))
+    rel_l2 = float((o - r).norm() / r.norm().clamp_min(1e-300))
+    rel_max = float((o - r).abs().max() / r.abs().max().clamp_min(1e-300))
+    return dict(cos=cos, rel_l2=rel_l2, rel_max=rel_max)

@@ -1,0 +1,123 @@
+"""The consumer check on the CPU: attention over the oracle's unpacked tensors, read the way
+the Sage consumer reads them (oracle/consumer.py), against float64 attention on the original
+Q, K, V (CPU only).
+
+Tolerance.  INT8 codes carry a rounding error of at most half a step (group amax/254)
+per element; E4M3 keeps 3 fraction bits, a relative rounding error of at most 2^-4 and
+about 2.4 % RMS on values spread over a binade.  The output is a softmax average of V rows
+whose signs vary, so the V rounding shows almost unchanged in the output, and scores of
+size O(1) add the Q/K rounding: 3.6-4.7 % relative L2 error (cosine similarity >= 0.9989)
+on normal inputs, 13.7 % (cosine 0.9906) on the heavy-tailed Student-t Q/V with outlier
+mean channels, whose group amax is set by rare large values.  Held to rel_l2 <= 0.2 and
+cos >= 0.98.  A consumer that misreads a layout or a scale is off by 150 % or more (cosine
+<= 0.75), which the second half of the file checks: each plausible misreading fails the
+same bounds.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+from oracle import consumer, pipeline
+from precision_attention_input_amd import workloads as W
+
+from helpers import small
+
+COS, REL = 0.98, 0.2
+
+
+def grouped_inputs(w, seed=0):
+    """Inputs in the smooth-K regime the method targets (K = per-channel mean + deviation),
+    with deviations of unit size so that scores are O(1), and with every 64-row group of Q
+    and of the K deviation scaled by its own factor in {1/2, 1, 2} (per head): the group
+    scales then differ, and a consumer using the wrong group's scale is visibly wrong."""
+    w = w.with_(eps_std=1.0)
+    d = W.generate(w)
+    g = torch.Generator().manual_seed(seed)
+    G = (w.S + 63) // 64
+    u = w.used or w.S
+
+    def factors():
+        f = torch.exp2(torch.randint(-1, 2, (w.B, G, w.H), generator=g).float())
+        return f.repeat_interleave(64, dim=1)[:, :w.S, :, None]
+
+    d["Q"] = (d["Q"].float() * factors()).to(w.dtype)
+    m = W.k_mean_global(d["K"], u, torch.float32)[:, None]
+    d["K"] = (m + (d["K"].float() - m) * factors()).to(w.dtype)
+    d["Q"][:, u:] = 0
+    d["K"][:, u:] = 0
+    d["mean"] = W.k_mean_global(d["K"], u, w.dtype)
+    return w, d
+
+
+def caller_v_scale(d, w):
+    """A caller's V scale: per (b, head, channel) max |V| over live rows / 448 (nonzero)."""
+    u = w.used or w.S
+    return (d["V"][:, :u].float().abs().amax(dim=1) / 448.0).clamp_min(2.0 ** -20)
+
+
+def worst(w, d, res, vs=None, reader=consumer.quantized_attention, nq=48):
+    used = w.used or w.S
+    qsel = sorted(set(list(range(0, used, max(1, used // nq))) + [used - 1]))
+    out = None
+    for p in range(w.P):
+        q8, k8, v8, qs, ks = res["outs"][p]
+        for b in range(w.B):
+            for j in range(w.h):
+                hh = p * w.h + j
+                o = reader(q8, k8, v8, qs, ks, b=b, j=j, queries=qsel, used=used,
+                           v_scale_row=None if vs is None else vs[b, hh])
+                r = consumer.reference_attention(d["Q"], d["K"], d["V"], b=b, head=hh,
+                                                 queries=qsel, used=used)
+                c = consumer.compare(o, r)
+                if out is None or c["rel_l2"] > out["rel_l2"]:
+                    out = c
+    return out
+
+
+CASES = [W.TINY, W.UNALIGNED_PADDED.with_(L=200, used=700, scale_sequence=700),
+         W.BATCHED_SMALL_HEAD.with_(B=2, L=256, H=8, used=400, scale_sequence=400),
+         small(P=8, L=100, H=8, D=128, dtype=torch.float16, used=777, seed=3)]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+@pytest.mark.parametrize("scaled", [False, True], ids=["unscaled_v", "caller_v_scale"])
+def test_consumer_matches_fp64_attention(olib, w, scaled):
+    w, d = grouped_inputs(w)
+    vs = caller_v_scale(d, w) if scaled else None
+    res = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                             used_sequence=w.used, scale_sequence=w.scale_sequence, v_scale=vs)
+    c = worst(w, d, res, vs)
+    assert c["cos"] >= COS and c["rel_l2"] <= REL, c
+
+
+# ----------------------------------------------------------------- misreadings must fail
+
+def _v_as_hd(q8, k8, v8, qs, ks, **kw):
+    B, D, h, sp = v8.shape
+    return consumer.quantized_attention(q8, k8, v8.reshape(B, h, D, sp).transpose(1, 2),
+                                        qs, ks, **kw)
+
+
+def _q_scale_first_group(q8, k8, v8, qs, ks, **kw):
+    return consumer.quantized_attention(q8, k8, v8, qs[:, :, :1].expand_as(qs), ks, **kw)
+
+
+def _k_scale_shifted(q8, k8, v8, qs, ks, **kw):
+    return consumer.quantized_attention(q8, k8, v8, qs, torch.roll(ks, 1, dims=2), **kw)
+
+
+def _v_rows_reversed_in_tile(q8, k8, v8, qs, ks, **kw):
+    sp = v8.shape[-1]
+    idx = torch.arange(sp).view(-1, 64).flip(1).flatten()
+    return consumer.quantized_attention(q8, k8, v8[..., idx], qs, ks, **kw)
+
+
+@pytest.mark.parametrize("reader", [_v_as_hd, _q_scale_first_group, _k_scale_shifted,
+                                    _v_rows_reversed_in_tile])
+def test_misread_layouts_fail_the_bounds(olib, reader):
+    w, d = grouped_inputs(CASES[2])
+    res = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                             used_sequence=w.used, scale_sequence=w.scale_sequence)
+    c = worst(w, d, res, reader=reader)
+    assert c["cos"] < COS or c["rel_l2"] > REL, c
