@@ -100,7 +100,8 @@ int64_t width_of(int64_t n) { return (n + ULP_GROUP_ROWS - 1) / ULP_GROUP_ROWS; 
 }  // namespace
 
 namespace ulp {
-int64_t unpack_blocks(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W);
+int64_t unpack_blocks(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W,
+                      int64_t ndests);
 }
 
 extern "C" {
@@ -229,7 +230,7 @@ static int unpack_common(const char* fn, const uint8_t* recv, int64_t B, int64_t
     TRY(check_ptr(fn, "q_scale", q_scale));
     TRY(check_ptr(fn, "k_scale", k_scale));
     const int64_t W = width_of(scale_sequence == ULP_NONE ? S : scale_sequence);
-    if (ulp::unpack_blocks(B, L, h, D, world_size, W) >= kMaxGrid)
+    if (ulp::unpack_blocks(B, L, h, D, world_size, W, ndests) >= kMaxGrid)
         return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
     const int64_t spad = (S + ULP_GROUP_ROWS - 1) / ULP_GROUP_ROWS * ULP_GROUP_ROWS;
     const int64_t cb = ulp::chunk_bytes_of(B, L, h, D);

@@ -25,7 +25,10 @@
 namespace ulp {
 namespace {
 
-constexpr int kCols = 32;                 // 16-element vectors per workgroup row
+#ifndef ULP_PACK_COLS
+#define ULP_PACK_COLS 32
+#endif
+constexpr int kCols = ULP_PACK_COLS;      // 16-element vectors per workgroup row
 constexpr int kRows = kThreads / kCols;   // rows per workgroup
 
 struct PackParams {

@@ -80,8 +80,13 @@ __device__ __forceinline__ void store16(void* p, const uint4& v) {
 // step finds it there (the pack re-reads Q and K right after the statistics pass; the
 // unpack reads the chunks the pack just wrote).  Larger streams cannot stay resident, and
 // non-temporal accesses then keep them from evicting data that can; the launchers pick the
-// instantiation from the stream's size.
-constexpr int64_t kResidentBytes = (int64_t)128 << 20;
+// instantiation from the stream's size.  The unpack's outputs, which nothing in the path
+// reads again, are always streamed.
+#ifndef ULP_RESIDENT_MB
+#define ULP_RESIDENT_MB 128
+#endif
+constexpr int64_t kResidentBytes = (int64_t)ULP_RESIDENT_MB << 20;
+
 
 // min(max(x, lo), hi) in one v_med3_f32 for finite lo <= hi.
 __device__ __forceinline__ float clampf(float x, float lo, float hi) {

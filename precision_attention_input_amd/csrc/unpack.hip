@@ -7,7 +7,7 @@
 //   q_scale, k_scale fp32 [B, h, W], W = ceil(n/64) for the consumer's live prefix n.
 // One launch does all three parts; each workgroup picks its part from its block index:
 //   * copy:  every (tensor, source, b) block of L*h*D bytes is contiguous on both sides, so
-//            it is a plain 16-byte vector copy (4 vectors per thread per workgroup);
+//            it is a plain 16-byte vector copy (2 or 8 vectors per thread per workgroup);
 //   * V:     each wave transposes a 16-row x 16-byte register block per lane: 16 coalesced
 //            16-byte loads along channels, 16 byte-level 4x4 transposes with v_perm_b32,
 //            16 coalesced 16-byte stores along time.  A wave covers 128 (D = 128) or 256
@@ -20,10 +20,19 @@
 namespace ulp {
 namespace {
 
-#ifndef ULP_UNPACK_COPY_UNROLL
-#define ULP_UNPACK_COPY_UNROLL 4
+// 16-byte vectors per thread of a copy workgroup, for launches whose received bytes stay
+// in the cache (small) and for those streamed from HBM (large).
+#ifndef ULP_UNPACK_UNROLL_SMALL
+#define ULP_UNPACK_UNROLL_SMALL 8
 #endif
-constexpr int kCopyUnroll = ULP_UNPACK_COPY_UNROLL;
+#ifndef ULP_UNPACK_UNROLL_LARGE
+#define ULP_UNPACK_UNROLL_LARGE 2
+#endif
+constexpr int kUnrollSmall = ULP_UNPACK_UNROLL_SMALL;
+constexpr int kUnrollLarge = ULP_UNPACK_UNROLL_LARGE;
+#ifndef ULP_UNPACK_V_ORDER
+#define ULP_UNPACK_V_ORDER 0
+#endif
 
 struct UnpackParams {
     const uint8_t* recv;
@@ -36,13 +45,21 @@ struct UnpackParams {
     int64_t copy_bps, n_copy, n_v, v_tiles;
 };
 
-template <int D, bool NT>
+// NTL: non-temporal loads of the received chunks.  UNROLL: 16-byte vectors per thread of a
+// copy workgroup.  Outputs are always stored non-temporally: they are not read again in
+// this path, and streaming stores measured faster than write-allocating ones at every size.
+template <int D, bool NTL, int UNROLL>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
-    const int64_t z = blockIdx.z;
-    const uint8_t* recv = p.recv + z * p.recv_dest_stride;
     const int tid = threadIdx.x;
-    int64_t bid = blockIdx.x;
     const int64_t L = p.L, h = p.h;
+    const int64_t z = blockIdx.z;
+    int64_t bid = blockIdx.x;
+    // Block order within a destination: V transposes first (their waves have the longest
+    // load -> transpose -> store chains), then copies, then scales.  Destinations follow
+    // one another, so transposes and copies of different destinations overlap.
+    if (bid < p.n_v) bid += p.n_copy;
+    else if (bid < p.n_v + p.n_copy) bid -= p.n_v;
+    const uint8_t* recv = p.recv + z * p.recv_dest_stride;
 
     if (bid < p.n_copy) {
         const int64_t seg = bid / p.copy_bps, part = bid % p.copy_bps;
@@ -50,16 +67,16 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         const int64_t s = (seg / p.B) % p.P, b = seg % p.B;
         const uint8_t* src = recv + s * p.cb + tensor * p.sec + b * L * h * D;
         int8_t* dst = (tensor ? p.k8 : p.q8) + z * p.qk_dest_stride + (b * p.S + s * L) * h * D;
-        uint4 v[kCopyUnroll];
+        uint4 v[UNROLL];
 #pragma unroll
-        for (int i = 0; i < kCopyUnroll; ++i) {
-            const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) v[i] = load16<true>(src + 16 * e);
+        for (int i = 0; i < UNROLL; ++i) {
+            const int64_t e = (part * UNROLL + i) * kThreads + tid;
+            if (e < p.seg_vecs) v[i] = load16<NTL>(src + 16 * e);
         }
 #pragma unroll
-        for (int i = 0; i < kCopyUnroll; ++i) {
-            const int64_t e = (part * kCopyUnroll + i) * kThreads + tid;
-            if (e < p.seg_vecs) store16<NT>(dst + 16 * e, v[i]);
+        for (int i = 0; i < UNROLL; ++i) {
+            const int64_t e = (part * UNROLL + i) * kThreads + tid;
+            if (e < p.seg_vecs) store16<true>(dst + 16 * e, v[i]);
         }
         return;
     }
@@ -69,10 +86,24 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         constexpr int DB = D / 16;             // 16-byte channel blocks per row
         constexpr int T = 16 * (64 / DB);      // time steps per wave tile
         const int wave = tid >> 6, lane = tid & 63;
+#if ULP_UNPACK_V_ORDER == 0
         const int64_t item = bid * 4 + wave;   // (b, head, tile)
         if (item >= p.B * h * p.v_tiles) return;
         const int64_t tile = item % p.v_tiles, bj = item / p.v_tiles;
         const int64_t j = bj % h, b = bj / h;
+#elif ULP_UNPACK_V_ORDER == 1
+        const int64_t item = bid * 4 + wave;   // (b, tile, head)
+        if (item >= p.B * h * p.v_tiles) return;
+        const int64_t j = item % h, bt = item / h;
+        const int64_t tile = bt % p.v_tiles, b = bt / p.v_tiles;
+#else
+        // workgroup = 4 consecutive tiles of one head; consecutive workgroups = the heads of
+        // the same rows
+        const int64_t ntg = (p.v_tiles + 3) / 4;
+        const int64_t j = bid % h, btg = bid / h;
+        const int64_t tile = (btg % ntg) * 4 + wave, b = btg / ntg;
+        if (tile >= p.v_tiles) return;
+#endif
         const int db = lane % DB, tb = lane / DB;
         const int64_t t0 = tile * T + tb * 16;
         if (t0 >= p.spad) return;
@@ -84,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             uint4 x = make_uint4(0, 0, 0, 0);
-            if (t0 + i < p.S) x = load16<true>(vsec + s * p.cb + l * h * D);
+            if (t0 + i < p.S) x = load16<NTL>(vsec + s * p.cb + l * h * D);
             w[i][0] = x.x;
             w[i][1] = x.y;
             w[i][2] = x.z;
@@ -104,7 +135,8 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         uint8_t* out = p.v8 + z * p.v_dest_stride + ((b * D + d0) * h + j) * p.spad + t0;
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc)
-            store16<NT>(out + (int64_t)cc * h * p.spad, make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
+            store16<true>(out + (int64_t)cc * h * p.spad,
+                          make_uint4(o[cc][0], o[cc][1], o[cc][2], o[cc][3]));
         return;
     }
     bid -= p.n_v;
@@ -120,8 +152,44 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         *reinterpret_cast<const float*>(c + p.ssec);
 }
 
+// Geometry of one unpack launch (shared by the launcher and the grid-size validation).
+struct UnpackGeometry {
+    bool nt_loads;
+    int unroll;
+    int64_t seg_vecs, copy_bps, n_copy, spad, v_tiles, n_v, n_scale;
+};
+
+UnpackGeometry unpack_geometry(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W,
+                               int64_t ndests) {
+    UnpackGeometry g;
+    // received bytes of the launch: streamed from HBM (non-temporal) when they exceed the
+    // cache budget, else read through the cache that the pack just wrote them into
+    g.nt_loads = ndests * P * chunk_bytes_of(B, L, h, D) > kResidentBytes;
+    g.unroll = g.nt_loads ? kUnrollLarge : kUnrollSmall;
+    g.seg_vecs = L * h * D / 16;
+    g.copy_bps = (g.seg_vecs + g.unroll * kThreads - 1) / (g.unroll * kThreads);
+    g.n_copy = 2 * P * B * g.copy_bps;
+    const int64_t S = P * L;
+    g.spad = (S + kGroup - 1) / kGroup * kGroup;
+    const int64_t T = 16 * (64 / (D / 16));
+    g.v_tiles = (g.spad + T - 1) / T;
+#if ULP_UNPACK_V_ORDER == 2
+    g.n_v = B * h * ((g.v_tiles + 3) / 4);
+#else
+    g.n_v = (B * h * g.v_tiles + 3) / 4;
+#endif
+    g.n_scale = (B * h * W + kThreads - 1) / kThreads;
+    return g;
+}
+
+template <int D, bool NTL, int UNROLL>
+void launch_v(const dim3& grid, hipStream_t stream, const UnpackParams& p) {
+    hipLaunchKernelGGL((unpack_kernel<D, NTL, UNROLL>), grid, dim3(kThreads), 0, stream, p);
+}
+
 template <int D>
 hipError_t launch_t(const UnpackLaunch& a, hipStream_t stream) {
+    const UnpackGeometry g = unpack_geometry(a.B, a.L, a.h, D, a.P, a.W, a.ndests);
     UnpackParams p;
     p.recv = a.recv;
     p.recv_dest_stride = a.recv_dest_stride;
@@ -138,27 +206,22 @@ hipError_t launch_t(const UnpackLaunch& a, hipStream_t stream) {
     p.h = a.h;
     p.P = a.P;
     p.S = a.P * a.L;
-    p.spad = (p.S + kGroup - 1) / kGroup * kGroup;
+    p.spad = g.spad;
     p.W = a.W;
     p.slots = slots_of(a.L);
     p.cb = chunk_bytes_of(a.B, a.L, a.h, D);
     p.sec = chunk_section(a.B, a.L, a.h, D);
     p.ssec = chunk_scale_section(a.B, a.L, a.h);
-    p.seg_vecs = a.L * a.h * D / 16;
-    p.copy_bps = (p.seg_vecs + kCopyUnroll * kThreads - 1) / (kCopyUnroll * kThreads);
-    p.n_copy = 2 * a.P * a.B * p.copy_bps;
-    constexpr int T = 16 * (64 / (D / 16));
-    p.v_tiles = (p.spad + T - 1) / T;
-    p.n_v = (a.B * a.h * p.v_tiles + 3) / 4;
-    const int64_t n_scale = (a.B * a.h * a.W + kThreads - 1) / kThreads;
-    dim3 grid((unsigned)(p.n_copy + p.n_v + n_scale), 1, (unsigned)a.ndests);
-    // the received chunks are read once (non-temporal); outputs stay cached when small, for
-    // the consumer that reads them next
-    const int64_t written = a.ndests * (2 * a.B * p.S * a.h * D + a.B * D * a.h * p.spad);
-    if (written > kResidentBytes)
-        hipLaunchKernelGGL((unpack_kernel<D, true>), grid, dim3(kThreads), 0, stream, p);
+    p.seg_vecs = g.seg_vecs;
+    p.copy_bps = g.copy_bps;
+    p.n_copy = g.n_copy;
+    p.v_tiles = g.v_tiles;
+    p.n_v = g.n_v;
+    dim3 grid((unsigned)(g.n_copy + g.n_v + g.n_scale), 1, (unsigned)a.ndests);
+    if (g.nt_loads)
+        launch_v<D, true, kUnrollLarge>(grid, stream, p);
     else
-        hipLaunchKernelGGL((unpack_kernel<D, false>), grid, dim3(kThreads), 0, stream, p);
+        launch_v<D, false, kUnrollSmall>(grid, stream, p);
     return hipGetLastError();
 }
 
@@ -169,13 +232,10 @@ hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream) {
 }
 
 // total blocks of one unpack launch (for validation of grid limits)
-int64_t unpack_blocks(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W) {
-    const int64_t seg_vecs = L * h * D / 16;
-    const int64_t bps = (seg_vecs + kCopyUnroll * kThreads - 1) / (kCopyUnroll * kThreads);
-    const int64_t S = P * L, spad = (S + kGroup - 1) / kGroup * kGroup;
-    const int64_t T = 16 * (64 / (D / 16));
-    const int64_t tiles = (spad + T - 1) / T;
-    return 2 * P * B * bps + (B * h * tiles + 3) / 4 + (B * h * W + kThreads - 1) / kThreads;
+int64_t unpack_blocks(int64_t B, int64_t L, int64_t h, int64_t D, int64_t P, int64_t W,
+                      int64_t ndests) {
+    const UnpackGeometry g = unpack_geometry(B, L, h, D, P, W, ndests);
+    return g.n_copy + g.n_v + g.n_scale;
 }
 
 }  // namespace ulp
