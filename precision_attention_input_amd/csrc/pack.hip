@@ -25,10 +25,7 @@
 namespace ulp {
 namespace {
 
-#ifndef ULP_PACK_COLS
-#define ULP_PACK_COLS 32
-#endif
-constexpr int kCols = ULP_PACK_COLS;      // 16-element vectors per workgroup row
+constexpr int kCols = 32;                 // 16-element vectors per workgroup row
 constexpr int kRows = kThreads / kCols;   // rows per workgroup
 
 struct PackParams {
@@ -157,8 +154,11 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     const uint4 q1 = load16(p.q + xo + 8);
     const uint4 k0 = load16(p.k + xo);
     const uint4 k1 = load16(p.k + xo + 8);
-    const uint4 v0 = load16(p.v + xo);
-    const uint4 v1 = load16(p.v + xo + 8);
+    // V is read once in the whole path: streamed, so that it does not evict the chunks this
+    // launch writes (which the unpack reads next) or Q and K (which the statistics pass
+    // just read).  Q and K keep the default policy, which measured faster at every size.
+    const uint4 v0 = load16<true>(p.v + xo);
+    const uint4 v1 = load16<true>(p.v + xo + 8);
     const uint16_t* mp = p.mean + ((uint64_t)b * H + head) * D + dv * 16;
     const uint4 m0 = load16(mp), m1 = load16(mp + 8);
     float4 sv[4];
