@@ -17,6 +17,11 @@
 namespace ulp {
 namespace {
 
+#ifndef ULP_STATS_ROWS_IN_FLIGHT
+#define ULP_STATS_ROWS_IN_FLIGHT 8
+#endif
+constexpr int kRowsInFlight = ULP_STATS_ROWS_IN_FLIGHT;
+
 struct StatsParams {
     const uint16_t* x[2];
     const uint16_t* mean[2];
@@ -81,12 +86,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
         decode8<DT>(load16(p.mean[tensor] + (b * H + head) * D + dv * 8), m);
 
     const uint16_t* xb = x + blockIdx.z * p.x_rank_stride + (b * L * H + head) * D + dv * 8;
-    uint4 v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t s = lo + rl + 8 * i;
-        v[i] = (valid && s < hi) ? load16<NT>(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
-    }
     float acc = -__builtin_inff();
     float mn[8], mx[8];
 #pragma unroll
@@ -94,22 +93,33 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
         mn[e] = __builtin_inff();
         mx[e] = -__builtin_inff();
     }
+    // 8 rows per thread, kRowsInFlight loads issued before each reduction batch
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t s = lo + rl + 8 * i;
-        if (!(valid && s < hi)) continue;
-        float f[8];
-        decode8<DT>(v[i], f);
-        if (want_amax && s < amax_hi) {
+    for (int i0 = 0; i0 < 8; i0 += kRowsInFlight) {
+        uint4 v[kRowsInFlight];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaxf(acc, __builtin_fabsf(f[e] - m[e]));
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int64_t s = lo + rl + 8 * (i0 + i);
+            v[i] = (valid && s < hi) ? load16<NT>(xb + (s - rank * L) * H * D)
+                                     : make_uint4(0, 0, 0, 0);
         }
-        if (want_mm && s < mm_hi) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float cv = f[e] + 0.0f;   // -0 -> +0, every other value unchanged
-                mn[e] = fminf(mn[e], cv);
-                mx[e] = fmaxf(mx[e], cv);
+        for (int i = 0; i < kRowsInFlight; ++i) {
+            const int64_t s = lo + rl + 8 * (i0 + i);
+            if (!(valid && s < hi)) continue;
+            float f[8];
+            decode8<DT>(v[i], f);
+            if (want_amax && s < amax_hi) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaxf(acc, __builtin_fabsf(f[e] - m[e]));
+            }
+            if (want_mm && s < mm_hi) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float cv = f[e] + 0.0f;   // -0 -> +0, every other value unchanged
+                    mn[e] = fminf(mn[e], cv);
+                    mx[e] = fmaxf(mx[e], cv);
+                }
             }
         }
     }
