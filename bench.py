@@ -146,6 +146,57 @@ def cpu_baseline(w, d, reps: int):
     return dt
 
 
+MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense int8 / fp8 matrix peak
+
+
+def consumer_bench(args, w, d, dev):
+    """K back-to-back launches of the consumer check over every destination's unpacked
+    tensors (one launch per destination), HIP events at the two ends."""
+    import torch
+
+    import precision_attention_input_amd as ulp
+    from precision_attention_input_amd import workloads as W
+
+    P, L, B, H, D = w.P, w.L, w.B, w.H, w.D
+    used = w.used or w.S
+    st = {n: W.stacked_shards(d[n], P).to(dev) for n in ("Q", "K", "V")}
+    mean = d["mean"].to(dev)
+    qa, ka, qm, km = ulp.group_stats(st["Q"], st["K"], mean, world_size=P, used_sequence=w.used)
+    ulp.group_derive(qa, ka, qm, km, mean, local_sequence=L, world_size=P)
+    grp = ulp.group_pack(st["Q"], st["K"], st["V"], mean, qa, ka, world_size=P)
+    outs = ulp.group_unpack(grp, batch_size=B, local_sequence=L, local_heads=w.h, head_dim=D,
+                            world_size=P, aligned=w.aligned, scale_sequence=w.scale_sequence)
+    res = [torch.empty(B, used, w.h, D, dtype=torch.float32, device=dev) for _ in range(P)]
+
+    def run():
+        for p in range(P):
+            ulp.consumer_attention(*(t[p] for t in outs), used=used, out=res[p])
+
+    for _ in range(args.warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (args.steps * P)          # one destination's launch
+    flops = 4.0 * B * w.h * used * used * D                # Q.K and P.V, per destination
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "consumer check attention TFLOP/s (INT8 Q.K + FP8 P.V on MFMA)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_launch": round(ms, 5), "higher_is_better": True,
+        "dtype": "i8/fp8", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "local_heads": w.h, "used_sequence": used,
+                   "head_dim": D, "launches_per_step": P},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                     "flops_per_launch": flops},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +207,10 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--consumer", action="store_true",
+                    help="time the MFMA consumer check (INT8 Q.K, FP8 P.V attention over every "
+                         "destination's unpacked tensors) instead of the path; prints its own "
+                         "JSON line (TFLOP/s against the 5.0 PFLOP/s int8/fp8 dense peak)")
     ap.add_argument("--v-scale", action="store_true",
                     help="pass a caller-held [B,H,D] V scale to the pack (V divided before "
                          "E4M3); the default converts V unscaled")
@@ -198,6 +253,9 @@ def main():
 
     w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
     d = W.generate(w)
+    if args.consumer:
+        consumer_bench(args, w, d, dev)
+        return
     nb = algorithmic_bytes(w, args.v_scale)
     vsc = W.v_scale(w).to(dev) if args.v_scale else None
     set_bytes = 12 * nb["N"]      # stacked Q/K/V (6N) + all-to-all buffer (3N) + outputs (3N)

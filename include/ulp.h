@@ -219,6 +219,28 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
                int world_size, int64_t used_sequence, void* workspace, int64_t workspace_bytes,
                float* mean_f32, void* mean_dtype, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * Consumer check (not a step of the pack/unpack path).  Attention over one destination's
+ * unpacked tensors, read the way the Sage consumer named by unpack_for_sage (description,
+ * Returns) reads them: for rows i, t < used,
+ *   score(i, t) = (q8[b,i,j,:] . k8[b,t,j,:]) * q_scale[b,j,i/64] * k_scale[b,j,t/64] / sqrt(D)
+ *   out[b,i,j,d] = sum_t softmax_t(score(i, .)) * e4m3(v8[b,d,j,t]) * (v_scale ? v_scale[b,j,d] : 1)
+ * INT8 Q.K on MFMA (exact integer dot products); P quantized to E4M3 after scaling by 448
+ * and P.V on FP8 MFMA with FP32 accumulation, so each probability carries a relative
+ * rounding error of at most 2^-4 (absolute 2^-18 in the subnormal range).  Softmax
+ * without a causal mask.
+ *   q8, k8     [B, S, h, D] int8;  v8 [B, D, h, Spad] E4M3 bytes, Spad = ceil(S/64)*64.
+ *   q_scale, k_scale [B, h, W] float with W >= ceil(used/64); these two need only 4-byte
+ *              alignment (a destination's slice of stacked scale tensors need not be
+ *              16-byte aligned).
+ *   v_scale    [B, h, D] float (this destination's heads) or NULL.
+ *   out        [B, used, h, D] float.
+ * D is 64 or 128; 1 <= used <= S. */
+int ulp_consumer_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           int64_t B, int64_t S, int64_t h, int64_t D, int64_t W,
+                           int64_t used, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

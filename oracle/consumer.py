@@ -29,10 +29,9 @@ def e4m3_values(v8: torch.Tensor) -> torch.Tensor:
     return v8.contiguous().view(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)
 
 
-def quantized_attention(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries, used: int,
-                        v_scale_row=None) -> torch.Tensor:
-    """Output rows [len(queries), D] of local head j of batch entry b, from one
-    destination's unpacked tensors (CPU).  Keys t < used; v_scale_row: optional [D]."""
+def _probabilities(q8, k8, q_scale, k_scale, b, j, queries, used):
+    """Unnormalized softmax weights exp(score - row max) [nq, used] and their row sums,
+    float64 (scores as defined in the module docstring)."""
     qi = torch.as_tensor(queries, dtype=torch.int64)
     D = q8.shape[-1]
     q = q8[b, qi, j].to(torch.float64)                       # [nq, D] integers
@@ -40,12 +39,45 @@ def quantized_attention(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries
     dots = q @ k.T                                           # exact: |sum| < 2^21
     keys = torch.arange(used)
     scores = dots * q_scale[b, j, qi // GROUP].double()[:, None] \
-        * k_scale[b, j, keys // GROUP].double()[None, :]
-    p = torch.softmax(scores / math.sqrt(D), dim=-1)
+        * k_scale[b, j, keys // GROUP].double()[None, :] / math.sqrt(D)
+    p = torch.exp(scores - scores.max(dim=-1, keepdim=True).values)
+    return p, p.sum(dim=-1, keepdim=True)
+
+
+def _values(v8, b, j, used, v_scale_row):
     v = e4m3_values(v8[b, :, j, :used]).T                    # [nk, D]
     if v_scale_row is not None:
         v = v * v_scale_row.double()[None, :]
-    return p @ v
+    return v
+
+
+def quantized_attention(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries, used: int,
+                        v_scale_row=None) -> torch.Tensor:
+    """Output rows [len(queries), D] of local head j of batch entry b, from one
+    destination's unpacked tensors (CPU).  Keys t < used; v_scale_row: optional [D]."""
+    p, l = _probabilities(q8, k8, q_scale, k_scale, b, j, queries, used)
+    return (p @ _values(v8, b, j, used, v_scale_row)) / l
+
+
+def fp8_probability_bound(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries,
+                          used: int, v_scale_row=None):
+    """(out, bound) [len(queries), D]: the attention above and a per-element bound on how far
+    a consumer that rounds each probability to E4M3 (after scaling it by 448, with any
+    running maximum m_run <= the row maximum) may land from it.  Rounding to E4M3 moves a
+    value by at most 2^-4 of itself in the normal range and by at most 2^-10 (half the
+    smallest subnormal step) below it, i.e. a probability p by at most
+    max(2^-4 p, 2^-10 / 448) <= max(2^-4 p, 2^-18) in units of the row maximum; scaling by
+    exp2(m_run - max) <= 1 only shrinks that.  So
+        |out_fp8 - out| <= sum_t max(2^-4 p_t, 2^-18) |v_t| / sum_t p_t,
+    plus binary32 arithmetic (scores, exponentials, FP32 accumulation of up to `used`
+    terms), held to 1e-3 of sum_t p_t |v_t| / sum_t p_t."""
+    p, l = _probabilities(q8, k8, q_scale, k_scale, b, j, queries, used)
+    v = _values(v8, b, j, used, v_scale_row)
+    out = (p @ v) / l
+    av = v.abs()
+    bound = (torch.maximum(p * 2.0 ** -4, torch.full_like(p, 2.0 ** -18)) @ av) / l \
+        + 1e-3 * (p @ av) / l
+    return out, bound
 
 
 def reference_attention(Q, K, V, *, b: int, head: int, queries, used: int) -> torch.Tensor:

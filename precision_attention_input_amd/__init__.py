@@ -22,6 +22,7 @@ __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
     "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
+    "consumer_attention",
     "unpack_shapes",
 ]
 
@@ -70,6 +71,8 @@ def lib():
                                  i32),
             "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
             "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
+            "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                        vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -309,3 +312,23 @@ def k_mean(k, *, world_size, used_sequence=None, workspace=None, out=None):
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _p(mf), _p(md), _stream(k)))
     return mf, md
+
+
+# ------------------------------------------------------------------------- consumer check
+
+def consumer_attention(q8, k8, v8, q_scale, k_scale, *, used, v_scale=None, out=None):
+    """Attention over one destination's unpacked tensors as the Sage consumer reads them
+    (INT8 Q.K, FP8 P.V on MFMA): q8, k8 [B,S,h,D] int8, v8 [B,D,h,Spad] E4M3, scales
+    [B,h,W], v_scale [B,h,D] or None -> out [B,used,h,D] float32."""
+    B, S, h, D = q8.shape
+    W = q_scale.shape[-1]
+    if v_scale is not None and (v_scale.dtype != torch.float32 or
+                                tuple(v_scale.shape) != (B, h, D)):
+        raise ValueError("v_scale must be float32 [B, h, D]")
+    if out is None:
+        out = torch.empty(B, used, h, D, dtype=torch.float32, device=q8.device)
+    _dev(q8, k8, v8, q_scale, k_scale, v_scale, out)
+    _check(lib().ulp_consumer_attention(_p(q8), _p(k8), _p(v8), _p(q_scale), _p(k_scale),
+                                        _p(v_scale), B, S, h, D, W, used, _p(out),
+                                        _stream(q8)))
+    return out

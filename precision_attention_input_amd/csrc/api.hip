@@ -72,10 +72,10 @@ int check_seq(const char* fn, const char* name, int64_t v, int64_t S) {
                 (long long)S, (long long)v);
 }
 
-int check_ptr(const char* fn, const char* name, const void* p) {
+int check_ptr(const char* fn, const char* name, const void* p, int align = 16) {
     if (p == nullptr) return fail(ULP_EINVAL, "%s: %s is NULL", fn, name);
-    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-        return fail(ULP_EALIGN, "%s: %s is not 16-byte aligned", fn, name);
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+        return fail(ULP_EALIGN, "%s: %s is not %d-byte aligned", fn, name, align);
     return ULP_OK;
 }
 
@@ -385,6 +385,43 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
     a.used = used_or_s(used_sequence, world_size * L);
     a.dtype = dtype;
     return launched(ulp::launch_kmean(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_consumer_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           int64_t B, int64_t S, int64_t h, int64_t D, int64_t W,
+                           int64_t used, float* out, void* stream) {
+    const char* fn = "ulp_consumer_attention";
+    if (D != 64 && D != 128)
+        return fail(ULP_EUNSUPPORTED, "%s: head_dim must be 64 or 128, got %lld", fn,
+                    (long long)D);
+    if (B < 1 || S < 1 || h < 1)
+        return fail(ULP_EINVAL, "%s: batch, sequence and heads must be >= 1", fn);
+    if (used < 1 || used > S)
+        return fail(ULP_EINVAL, "%s: used must be in [1, %lld], got %lld", fn, (long long)S,
+                    (long long)used);
+    if (W < width_of(used))
+        return fail(ULP_EINVAL, "%s: scale width %lld < ceil(used / 64) = %lld", fn,
+                    (long long)W, (long long)width_of(used));
+    if (B > 65535 || h > 65535 || B * S > ((int64_t)1 << 40) / (h * D))
+        return fail(ULP_EINVAL, "%s: problem too large", fn);
+    TRY(check_ptr(fn, "q8", q8));
+    TRY(check_ptr(fn, "k8", k8));
+    TRY(check_ptr(fn, "v8", v8));
+    TRY(check_ptr(fn, "q_scale", q_scale, 4));   // read one float at a time
+    TRY(check_ptr(fn, "k_scale", k_scale, 4));
+    if (v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
+    TRY(check_ptr(fn, "out", out));
+    ulp::ConsumerLaunch a{};
+    a.q8 = q8;
+    a.k8 = k8;
+    a.v8 = v8;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.out = out;
+    a.B = B; a.S = S; a.h = h; a.D = D; a.W = W; a.used = used;
+    return launched(ulp::launch_consumer(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

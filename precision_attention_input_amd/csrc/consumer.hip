@@ -1,0 +1,183 @@
+// consumer.hip -- attention over one destination's unpacked tensors (gfx950 MFMA).
+//
+// A check of the unpacked layouts from the consumer's side, not a step of the pack/unpack
+// path: the unpack_for_sage page hands q8, k8 (INT8 [B, S, h, D], one FP32 scale per
+// 64-row group in q_scale / k_scale [B, h, W]) and v8 (FP8 E4M3 [B, D, h, Spad]) to a Sage
+// attention kernel, the V scale staying with the caller (Returns).  This kernel reads them
+// that way over the live rows t < used:
+//   score(i, t) = (q8[i] . k8[t]) * q_scale[i / 64] * k_scale[t / 64] / sqrt(D)
+//   out[i, d]   = sum_t softmax_t(score(i, .)) * e4m3(v8[d, t]) * v_scale[d]
+// with the INT8 dot products on v_mfma_i32_16x16x32_i8 (exact int32) and the P.V product on
+// v_mfma_f32_16x16x32_fp8_fp8, P quantized to E4M3 after scaling by 448 (the largest E4M3
+// value), as an FP8 consumer does.  Smooth K needs no correction: removing a per-channel
+// mean from every key shifts all scores of a query by the same amount.
+//
+// Work decomposition: a 256-thread workgroup owns 64 query rows of one (b, head) -- one Q
+// scale group -- and each wave 16 of them.  Both products are computed transposed, so that
+// every per-query quantity lives in the lanes of that query's column:
+//   S^T[key, q] = K . Q^T   (A = 16 keys x 32 channels of k8, B = 32 channels x 16 queries)
+//   O^T[d, q]  += V^T . P^T (A = 16 channels x 32 keys of v8, B = 32 keys x 16 queries)
+// Lane l of an MFMA operand holds row / column l % 16 and k-slice 8 * (l / 16) + [0, 8); the
+// accumulator lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16.  The keys of the P.V
+// product are taken in the order the S^T accumulators hold them (a permutation of the 32
+// keys applied identically to the V^T rows), so no data moves between lanes except the
+// max / sum reductions over the four lanes of a query.  Keys are processed 64 at a time
+// (one K scale group) with the running-max softmax.
+#include <cmath>
+
+#include "ulp_device.h"
+#include "ulp_kernels.h"
+
+namespace ulp {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+struct ConsumerParams {
+    const int8_t *q8, *k8;
+    const uint8_t* v8;
+    const float *q_scale, *k_scale, *v_scale;
+    float* out;
+    int64_t S, h, spad, W, used;
+    float score_scale;   // log2(e) / sqrt(D)
+};
+
+__device__ __forceinline__ int64_t load8(const int8_t* p) {
+    return *reinterpret_cast<const int64_t*>(p);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
+    constexpr int KC = D / 32;   // 32-channel slices of a Q / K row
+    constexpr int CB = D / 16;   // 16-channel blocks of the output
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int64_t tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+    const int64_t hD = p.h * D;
+    const int64_t qi = tile * 64 + wave * 16 + col;   // this lane's query
+
+    // Q^T fragments (B operand): channels 32c + 8 grp + [0, 8) of query qi.
+    int64_t qf[KC];
+    const int8_t* qrow = p.q8 + (b * p.S + qi) * hD + j * D + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[c] = qi < p.S ? load8(qrow + 32 * c) : 0;
+    const float qs = p.q_scale[(b * p.h + j) * p.W + tile] * p.score_scale;
+
+    v4f o[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) o[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -__builtin_inff(), lsum = 0.0f;
+
+    const int64_t ntiles = (p.used + 63) / 64;
+    const int8_t* kbase = p.k8 + b * p.S * hD + j * D + 8 * grp;
+    const uint8_t* vbase = p.v8 + ((b * D + col) * p.h + j) * p.spad + 4 * grp;
+    const int64_t vstride16 = 16 * p.h * p.spad;     // 16 channels further down
+    for (int64_t kt = 0; kt < ntiles; ++kt) {
+        const int64_t t0 = kt * 64;
+        // S^T for keys t0 + 16 kb + [0, 16): lane holds keys t0 + 16 kb + 4 grp + r.
+        v4i s[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int64_t t = t0 + 16 * kb + col;    // A row of this lane
+            const int8_t* krow = kbase + t * hD;
+            int64_t kf[KC];
+#pragma unroll
+            for (int c = 0; c < KC; ++c) kf[c] = t < p.used ? load8(krow + 32 * c) : 0;
+            s[kb] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                s[kb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(kf[c], qf[c], s[kb], 0, 0, 0);
+        }
+        const float sc = qs * p.k_scale[(b * p.h + j) * p.W + kt];
+        float x[4][4];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = t0 + 16 * kb + 4 * grp + r;
+                x[kb][r] = t < p.used ? (float)s[kb][r] * sc : -__builtin_inff();
+                tmax = fmaxf(tmax, x[kb][r]);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        float psum = 0.0f;
+        uint32_t pw[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+                psum += pr[r];
+            }
+            pw[kb] = e4m3x4(448.0f * pr[0], 448.0f * pr[1], 448.0f * pr[2], 448.0f * pr[3]);
+        }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        lsum = lsum * alpha + psum;
+        m = mnew;
+        // P^T fragments: keys (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp + [0, 4)).
+        const int64_t pf0 = (int64_t)pw[0] | ((int64_t)pw[1] << 32);
+        const int64_t pf1 = (int64_t)pw[2] | ((int64_t)pw[3] << 32);
+        const uint8_t* vt = vbase + t0;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint8_t* vr = vt + cb * vstride16;
+            const uint32_t* v32 = reinterpret_cast<const uint32_t*>(vr);
+            const int64_t va0 = (int64_t)v32[0] | ((int64_t)v32[4] << 32);    // keys +0, +16
+            const int64_t va1 = (int64_t)v32[8] | ((int64_t)v32[12] << 32);   // keys +32, +48
+            v4f acc = o[cb] * alpha;
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va0, pf0, acc, 0, 0, 0);
+            o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va1, pf1, acc, 0, 0, 0);
+        }
+    }
+
+    if (qi >= p.used) return;
+    const float inv = 1.0f / (448.0f * lsum);
+    float* orow = p.out + (b * p.used + qi) * hD + j * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int d0 = cb * 16 + 4 * grp;
+        float4 r = make_float4(o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv);
+        if (p.v_scale) {
+            const float4 vs =
+                *reinterpret_cast<const float4*>(p.v_scale + (b * p.h + j) * D + d0);
+            r.x *= vs.x;
+            r.y *= vs.y;
+            r.z *= vs.z;
+            r.w *= vs.w;
+        }
+        *reinterpret_cast<float4*>(orow + d0) = r;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream) {
+    ConsumerParams p;
+    p.q8 = a.q8;
+    p.k8 = a.k8;
+    p.v8 = a.v8;
+    p.q_scale = a.q_scale;
+    p.k_scale = a.k_scale;
+    p.v_scale = a.v_scale;
+    p.out = a.out;
+    p.S = a.S;
+    p.h = a.h;
+    p.spad = (a.S + kGroup - 1) / kGroup * kGroup;
+    p.W = a.W;
+    p.used = a.used;
+    p.score_scale = (float)(1.4426950408889634 / std::sqrt((double)a.D));
+    dim3 grid((unsigned)((a.used + 63) / 64), (unsigned)a.h, (unsigned)a.B);
+    if (a.D == 64)
+        hipLaunchKernelGGL((consumer_kernel<64>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((consumer_kernel<128>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace ulp

@@ -60,12 +60,23 @@ struct KMeanLaunch {
     int dtype;
 };
 
+// Attention over one destination's unpacked tensors (the consumer check).
+struct ConsumerLaunch {
+    const int8_t *q8, *k8;         // [B, S, h, D]
+    const uint8_t* v8;             // [B, D, h, Spad] E4M3
+    const float *q_scale, *k_scale;   // [B, h, W]
+    const float* v_scale;          // [B, h, D] or nullptr
+    float* out;                    // [B, used, h, D]
+    int64_t B, S, h, D, W, used;
+};
+
 // Rows per partial sum of the K mean, and the number of such chunks (workspace rows).
 int64_t kmean_rows(int64_t B, int64_t H, int64_t D, int64_t used);
 int64_t kmean_chunks(int64_t B, int64_t H, int64_t D, int64_t used);
 
 hipError_t launch_stats(const StatsLaunch& a, hipStream_t stream);
 hipError_t launch_kmean(const KMeanLaunch& a, hipStream_t stream);
+hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream);
 hipError_t launch_derive(const DeriveLaunch& a, hipStream_t stream);
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream);

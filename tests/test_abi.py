@@ -165,3 +165,15 @@ def test_k_mean_validation(L):
     assert call(md=A + 2) == EALIGN
     assert call(ws=0) == EINVAL
     assert call(B=70000, wsb=1 << 40) == EINVAL and b"too large" in L.ulp_last_error()
+
+
+def test_consumer_validation(L):
+    def call(B=1, S=128, h=2, D=64, W=2, used=128, v=None):
+        return L.ulp_consumer_attention(A, A, A, A, A, v, B, S, h, D, W, used, A, None)
+    assert call(D=96) == EUNSUPPORTED
+    assert call(used=0) == EINVAL and b"used" in L.ulp_last_error()
+    assert call(used=129) == EINVAL
+    assert call(W=1) == EINVAL and b"scale width" in L.ulp_last_error()
+    assert call(h=0) == EINVAL
+    assert call(v=A + 4) == EALIGN
+    assert L.ulp_consumer_attention(A, 0, A, A, A, None, 1, 128, 2, 64, 2, 128, A, None) == EINVAL

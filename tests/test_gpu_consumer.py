@@ -10,7 +10,10 @@ import torch
 
 from precision_attention_input_amd import workloads as W
 
+import precision_attention_input_amd as ulp
+
 from gpu_helpers import DEV, run_group, say, to_dev
+from helpers import small
 from test_oracle_consumer import COS, REL, caller_v_scale, grouped_inputs
 from oracle import consumer
 
@@ -42,3 +45,81 @@ def test_consumer_on_gpu_outputs(olib, wname):
                 worst = c
     say(f"[consumer] {wname}: worst {worst}")
     assert worst["cos"] >= COS and worst["rel_l2"] <= REL, worst
+
+
+# ----------------------------------------------------------------- the MFMA consumer kernel
+
+# Against attention on the original inputs the FP8 consumer carries, besides the input
+# quantization the exact consumer already shows (bounds COS, REL), the rounding of every
+# probability to E4M3: up to 2^-4 of each weight (the per-element bound below), about
+# 0.06 relative in the worst case.  Held to 0.2 + 0.06 + margin and a cosine 0.01 lower;
+# misread layouts or scales give >= 150 % (tests/test_oracle_consumer.py).
+COS_FP8, REL_FP8 = 0.97, 0.3
+
+def _check_mfma_consumer(w, d, g, vs, dests, heads_of, nq, label):
+    used = w.used or w.S
+    qsel = sorted(set(list(range(0, used, max(1, used // nq))) + [used - 1, used // 2]))
+    worst, e2e = 0.0, None
+    for p in dests:
+        q8, k8, v8, qs, ks = g["outs"][p]
+        vsp = None if vs is None else vs[:, p * w.h:(p + 1) * w.h].contiguous().to(DEV)
+        out = ulp.consumer_attention(q8, k8, v8, qs, ks, used=used, v_scale=vsp)
+        torch.cuda.synchronize()
+        out = out.cpu()
+        c8 = [t.cpu() for t in (q8, k8, v8, qs, ks)]
+        for b in range(w.B):
+            for j in heads_of(p):
+                hh = p * w.h + j
+                row = None if vs is None else vs[b, hh]
+                ref, bound = consumer.fp8_probability_bound(*c8, b=b, j=j, queries=qsel,
+                                                            used=used, v_scale_row=row)
+                got = out[b, qsel, j].double()
+                ratio = ((got - ref).abs() / bound).max().item()
+                assert ratio <= 1.0, f"{label}: dest {p} b {b} head {j}: error/bound {ratio}"
+                worst = max(worst, ratio)
+                c = consumer.compare(got, consumer.reference_attention(
+                    d["Q"], d["K"], d["V"], b=b, head=hh, queries=qsel, used=used))
+                if e2e is None or c["rel_l2"] > e2e["rel_l2"]:
+                    e2e = c
+        assert torch.isfinite(out).all()
+    say(f"[mfma consumer] {label}: worst error/bound {worst:.3f}, vs inputs {e2e}")
+    assert e2e["cos"] >= COS_FP8 and e2e["rel_l2"] <= REL_FP8, e2e
+
+
+@pytest.mark.parametrize("wname", [w.name for w in W.WORKLOADS])
+def test_mfma_consumer_within_fp8_bound(olib, wname):
+    """The gfx950 MFMA consumer (INT8 Q.K, FP8 P.V) on the HIP path's unpacked tensors, every
+    element of sampled query rows within the FP8-probability bound of the float64 consumer
+    (oracle/consumer.py), with a caller V scale on the fp16 workloads."""
+    w, d = grouped_inputs(W.BY_NAME[wname])
+    vs = caller_v_scale(d, w) if w.dtype == torch.float16 else None
+    dd = to_dev(d, w.P)
+    g = run_group(w, dd, w.aligned, v_scale=None if vs is None else vs.to(DEV))
+    big = w.S > 10000
+    dests = [0, w.P - 1] if big else list(range(w.P))
+    heads_of = (lambda p: [0, w.h - 1]) if big else (lambda p: range(w.h))
+    _check_mfma_consumer(w, d, g, vs, dests, heads_of, 12 if big else 40, wname)
+
+
+@pytest.mark.parametrize("P,L,H,D,used", [(2, 1, 2, 64, 1), (2, 33, 4, 128, 50),
+                                          (4, 100, 8, 64, 257), (8, 40, 8, 128, 320),
+                                          (2, 96, 2, 128, 130)])
+def test_mfma_consumer_edges(olib, P, L, H, D, used):
+    """One live row, used below / at / just past a 64-row group, S not a multiple of 64."""
+    w, d = grouped_inputs(small(B=2, P=P, L=L, H=H, D=D, dtype=torch.float16, used=used,
+                                scale_sequence=used, seed=used))
+    vs = caller_v_scale(d, w)
+    dd = to_dev(d, w.P)
+    g = run_group(w, dd, v_scale=vs.to(DEV))
+    _check_mfma_consumer(w, d, g, vs, range(w.P), lambda p: range(w.h), 64, w.name)
+
+
+def test_mfma_consumer_rejects_bad_arguments(olib):
+    """Validation happens before any launch (no kernel runs on these)."""
+    q8 = torch.zeros(1, 64, 2, 64, dtype=torch.int8, device=DEV)
+    v8 = torch.zeros(1, 64, 2, 64, dtype=torch.uint8, device=DEV)
+    sc = torch.ones(1, 2, 1, device=DEV)
+    with pytest.raises(ValueError, match="used"):
+        ulp.consumer_attention(q8, q8, v8, sc, sc, used=65)
+    with pytest.raises(ValueError, match="v_scale"):
+        ulp.consumer_attention(q8, q8, v8, sc, sc, used=64, v_scale=torch.ones(1, 2, 32, device=DEV))

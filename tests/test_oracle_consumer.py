@@ -121,3 +121,59 @@ def test_misread_layouts_fail_the_bounds(olib, reader):
                              used_sequence=w.used, scale_sequence=w.scale_sequence)
     c = worst(w, d, res, reader=reader)
     assert c["cos"] < COS or c["rel_l2"] > REL, c
+
+
+# ----------------------------------------------------------------- the FP8-probability bound
+
+def _simulated_fp8_consumer(q8, k8, v8, qs, ks, b, j, queries, used, vs=None):
+    """A tile-by-tile (64 keys) running-maximum softmax whose probabilities are rounded to
+    E4M3 after scaling by 448 (torch's float8 conversion), in float64 otherwise: what an
+    FP8 consumer computes, up to binary32 rounding."""
+    qi = torch.as_tensor(queries)
+    D = q8.shape[-1]
+    s = (q8[b, qi, j].double() @ k8[b, :used, j].double().T) \
+        * qs[b, j, qi // 64].double()[:, None] \
+        * ks[b, j, torch.arange(used) // 64].double()[None, :] / D ** 0.5
+    v = consumer.e4m3_values(v8[b, :, j, :used]).T
+    if vs is not None:
+        v = v * vs.double()[None, :]
+    m = torch.full((len(qi), 1), -float("inf"), dtype=torch.float64)
+    l = torch.zeros(len(qi), 1, dtype=torch.float64)
+    o = torch.zeros(len(qi), D, dtype=torch.float64)
+    for t0 in range(0, used, 64):
+        st = s[:, t0:t0 + 64]
+        mn = torch.maximum(m, st.max(dim=1, keepdim=True).values)
+        a = torch.exp(m - mn)
+        p = torch.exp(st - mn)
+        p8 = (448.0 * p).float().clamp(max=448.0).to(torch.float8_e4m3fn).double() / 448.0
+        l = l * a + p.sum(dim=1, keepdim=True)
+        o = o * a + p8 @ v[t0:t0 + 64]
+        m = mn
+    return o / l
+
+
+@pytest.mark.parametrize("w", CASES[:3], ids=[w.name for w in CASES[:3]])
+def test_fp8_probability_bound_holds_and_is_tight(olib, w):
+    """The bound of oracle.consumer.fp8_probability_bound contains a simulated FP8 consumer
+    everywhere, and is not vacuous: the worst element uses a visible part of it."""
+    w, d = grouped_inputs(w)
+    vs = caller_v_scale(d, w)
+    res = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                             used_sequence=w.used, scale_sequence=w.scale_sequence, v_scale=vs)
+    used = w.used or w.S
+    qsel = sorted(set(list(range(0, used, max(1, used // 32))) + [used - 1]))
+    worst = 0.0
+    for p in range(w.P):
+        q8, k8, v8, qs, ks = res["outs"][p]
+        for b in range(w.B):
+            for j in range(w.h):
+                row = vs[b, p * w.h + j]
+                out, bound = consumer.fp8_probability_bound(q8, k8, v8, qs, ks, b=b, j=j,
+                                                            queries=qsel, used=used,
+                                                            v_scale_row=row)
+                sim = _simulated_fp8_consumer(q8, k8, v8, qs, ks, b, j, qsel, used, row)
+                ratio = ((sim - out).abs() / bound).max().item()
+                assert ratio <= 1.0, (p, b, j, ratio)
+                worst = max(worst, ratio)
+    print(f"worst error / bound {worst:.3f}")
+    assert worst > 0.02, worst
