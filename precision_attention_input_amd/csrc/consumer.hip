@@ -13,7 +13,10 @@
 // mean from every key shifts all scores of a query by the same amount.
 //
 // Work decomposition: a 256-thread workgroup owns 64 query rows of one (b, head) -- one Q
-// scale group -- and each wave 16 of them.  Both products are computed transposed, so that
+// scale group -- and each wave 16 of them.  Key tiles of 64 rows (one K scale group) and the
+// matching 64 columns of v8 are copied with coalesced 16-byte loads into double-buffered LDS
+// tiles shared by the four waves; the next tile's loads are in flight while the current one
+// is computed.  Both products are computed transposed, so that
 // every per-query quantity lives in the lanes of that query's column:
 //   S^T[key, q] = K . Q^T   (A = 16 keys x 32 channels of k8, B = 32 channels x 16 queries)
 //   O^T[d, q]  += V^T . P^T (A = 16 channels x 32 keys of v8, B = 32 keys x 16 queries)
@@ -47,11 +50,29 @@ __device__ __forceinline__ int64_t load8(const int8_t* p) {
     return *reinterpret_cast<const int64_t*>(p);
 }
 
+// LDS tiles: 64 keys x D channels of k8 and D channels x 64 keys of v8, rows padded by 16
+// bytes (keeps 16-byte writes aligned and spreads the fragment reads over the banks).
+template <int D>
+struct ConsumerTiles {
+    static constexpr int KROW = D + 16, VROW = 64 + 16;
+    static constexpr int KBYTES = 64 * KROW, VBYTES = D * VROW;
+    uint8_t k[2][KBYTES];
+    uint8_t v[2][VBYTES];
+};
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
     constexpr int KC = D / 32;   // 32-channel slices of a Q / K row
     constexpr int CB = D / 16;   // 16-channel blocks of the output
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using T = ConsumerTiles<D>;
+    // global -> LDS copy of one tile: 16 bytes per thread per step
+    constexpr int KV = D / 16;                 // 16-byte pieces of a K row
+    constexpr int KSTEPS = 64 * KV / kThreads; // K tile: 64 rows
+    constexpr int VSTEPS = D * 4 / kThreads;   // V tile: D rows of 4 pieces
+    __shared__ __align__(16) T tl;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const int64_t tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int64_t hD = p.h * D;
@@ -70,24 +91,59 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
     float m = -__builtin_inff(), lsum = 0.0f;
 
     const int64_t ntiles = (p.used + 63) / 64;
-    const int8_t* kbase = p.k8 + b * p.S * hD + j * D + 8 * grp;
-    const uint8_t* vbase = p.v8 + ((b * D + col) * p.h + j) * p.spad + 4 * grp;
-    const int64_t vstride16 = 16 * p.h * p.spad;     // 16 channels further down
+    const int8_t* kg = p.k8 + b * p.S * hD + j * D;
+    const uint8_t* vg = p.v8 + ((b * D) * p.h + j) * p.spad;
+    const int64_t vrow = p.h * p.spad;         // bytes between channel rows of v8
+
+    // Coalesced tile loads into registers (rows of k8 are 16-byte pieces of D bytes; rows
+    // of the tile's v8 are 64 bytes of one channel).  K rows past `used` are zero.
+    uint4 kr[KSTEPS], vr[VSTEPS];
+    auto fetch = [&](int64_t t0) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int e = s * kThreads + tid, row = e / KV, piece = e % KV;
+            const int64_t t = t0 + row;
+            kr[s] = t < p.used ? *reinterpret_cast<const uint4*>(kg + t * hD + 16 * piece)
+                               : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < VSTEPS; ++s) {
+            const int e = s * kThreads + tid, d = e / 4, piece = e % 4;
+            vr[s] = *reinterpret_cast<const uint4*>(vg + d * vrow + t0 + 16 * piece);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            const int e = s * kThreads + tid, row = e / KV, piece = e % KV;
+            *reinterpret_cast<uint4*>(&tl.k[buf][row * T::KROW + 16 * piece]) = kr[s];
+        }
+#pragma unroll
+        for (int s = 0; s < VSTEPS; ++s) {
+            const int e = s * kThreads + tid, d = e / 4, piece = e % 4;
+            *reinterpret_cast<uint4*>(&tl.v[buf][d * T::VROW + 16 * piece]) = vr[s];
+        }
+    };
+    fetch(0);
+    stash(0);
+    __syncthreads();
+
     for (int64_t kt = 0; kt < ntiles; ++kt) {
+        const int buf = (int)(kt & 1);
         const int64_t t0 = kt * 64;
+        if (kt + 1 < ntiles) fetch(t0 + 64);   // in flight while this tile is computed
+        const uint8_t* kl = tl.k[buf];
+        const uint8_t* vl = tl.v[buf];
         // S^T for keys t0 + 16 kb + [0, 16): lane holds keys t0 + 16 kb + 4 grp + r.
         v4i s[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int64_t t = t0 + 16 * kb + col;    // A row of this lane
-            const int8_t* krow = kbase + t * hD;
-            int64_t kf[KC];
-#pragma unroll
-            for (int c = 0; c < KC; ++c) kf[c] = t < p.used ? load8(krow + 32 * c) : 0;
             s[kb] = v4i{0, 0, 0, 0};
+            const uint8_t* krow = kl + (16 * kb + col) * T::KROW + 8 * grp;
 #pragma unroll
             for (int c = 0; c < KC; ++c)
-                s[kb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(kf[c], qf[c], s[kb], 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
+                    *reinterpret_cast<const int64_t*>(krow + 32 * c), qf[c], s[kb], 0, 0, 0);
         }
         const float sc = qs * p.k_scale[(b * p.h + j) * p.W + kt];
         float x[4][4];
@@ -120,20 +176,22 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
         psum += __shfl_xor(psum, 32, 64);
         lsum = lsum * alpha + psum;
         m = mnew;
-        // P^T fragments: keys (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp + [0, 4)).
+        // P^T fragments: keys (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp + [0, 4)),
+        // and the V^T rows (channels) in the same key order.
         const int64_t pf0 = (int64_t)pw[0] | ((int64_t)pw[1] << 32);
         const int64_t pf1 = (int64_t)pw[2] | ((int64_t)pw[3] << 32);
-        const uint8_t* vt = vbase + t0;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const uint8_t* vr = vt + cb * vstride16;
-            const uint32_t* v32 = reinterpret_cast<const uint32_t*>(vr);
+            const uint32_t* v32 =
+                reinterpret_cast<const uint32_t*>(vl + (16 * cb + col) * T::VROW + 4 * grp);
             const int64_t va0 = (int64_t)v32[0] | ((int64_t)v32[4] << 32);    // keys +0, +16
             const int64_t va1 = (int64_t)v32[8] | ((int64_t)v32[12] << 32);   // keys +32, +48
             v4f acc = o[cb] * alpha;
             acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va0, pf0, acc, 0, 0, 0);
             o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va1, pf1, acc, 0, 0, 0);
         }
+        if (kt + 1 < ntiles) stash(buf ^ 1);   // the other buffer: nobody reads it now
+        __syncthreads();
     }
 
     if (qi >= p.used) return;
