@@ -228,7 +228,7 @@ def main():
         record_traffic(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (the whole Ulysses group is held "
+        print(f"bench.py: runs on one GPU only (the whole Ulysses group is held "
               f"by one device; world_size only shapes the byte layout); --gpus {args.gpus} "
               f"is not supported", file=sys.stderr)
         sys.exit(2)

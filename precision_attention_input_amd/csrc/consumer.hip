@@ -50,6 +50,28 @@ __device__ __forceinline__ int64_t load8(const int8_t* p) {
     return *reinterpret_cast<const int64_t*>(p);
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's lanes), left in all
+// four, with gfx950's lane-swap instructions: v_permlane16_swap exchanges rows 1 and 3 of one
+// register with rows 0 and 2 of another, v_permlane32_swap the upper half of one with the
+// lower half of another; both operands are copies of v, so each result lane meets its
+// partner's value.  No LDS traffic.  The sum is (r0 + r1) + (r2 + r3) in every lane.
+__device__ __forceinline__ float quad_max(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(v);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned w = __float_as_uint(v);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // LDS tiles: 64 keys x D channels of k8 and D channels x 64 keys of v8, rows padded by 16
 // bytes (keeps 16-byte writes aligned and spreads the fragment reads over the banks).
 template <int D>
@@ -156,8 +178,7 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
                 x[kb][r] = t < p.used ? (float)s[kb][r] * sc : -__builtin_inff();
                 tmax = fmaxf(tmax, x[kb][r]);
             }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = quad_max(tmax);
         const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         float psum = 0.0f;
@@ -172,8 +193,7 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
             }
             pw[kb] = e4m3x4(448.0f * pr[0], 448.0f * pr[1], 448.0f * pr[2], 448.0f * pr[3]);
         }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
+        psum = quad_sum(psum);
         lsum = lsum * alpha + psum;
         m = mnew;
         // P^T fragments: keys (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp + [0, 4)),
