@@ -37,6 +37,11 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+#ifndef ULP_CONSUMER_KEYS
+#define ULP_CONSUMER_KEYS 128
+#endif
+constexpr int kConsumerKeys = ULP_CONSUMER_KEYS;   // keys per LDS tile: 64 or 128
+
 struct ConsumerParams {
     const int8_t *q8, *k8;
     const uint8_t* v8;
@@ -72,25 +77,29 @@ __device__ __forceinline__ float quad_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// LDS tiles: 64 keys x D channels of k8 and D channels x 64 keys of v8, rows padded by 16
+// LDS tiles: KT keys x D channels of k8 and D channels x KT keys of v8, rows padded by 16
 // bytes (keeps 16-byte writes aligned and spreads the fragment reads over the banks).
-template <int D>
+template <int D, int KT>
 struct ConsumerTiles {
-    static constexpr int KROW = D + 16, VROW = 64 + 16;
-    static constexpr int KBYTES = 64 * KROW, VBYTES = D * VROW;
+    static constexpr int KROW = D + 16, VROW = KT + 16;
+    static constexpr int KBYTES = KT * KROW, VBYTES = D * VROW;
     uint8_t k[2][KBYTES];
     uint8_t v[2][VBYTES];
 };
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
-    constexpr int KC = D / 32;   // 32-channel slices of a Q / K row
-    constexpr int CB = D / 16;   // 16-channel blocks of the output
-    using T = ConsumerTiles<D>;
+    constexpr int KT = kConsumerKeys;          // keys per tile
+    constexpr int KB = KT / 16;                // 16-key blocks of S^T per tile
+    constexpr int KC = D / 32;                 // 32-channel slices of a Q / K row
+    constexpr int CB = D / 16;                 // 16-channel blocks of the output
+    using T = ConsumerTiles<D, KT>;
     // global -> LDS copy of one tile: 16 bytes per thread per step
     constexpr int KV = D / 16;                 // 16-byte pieces of a K row
-    constexpr int KSTEPS = 64 * KV / kThreads; // K tile: 64 rows
-    constexpr int VSTEPS = D * 4 / kThreads;   // V tile: D rows of 4 pieces
+    constexpr int VV = KT / 16;                // 16-byte pieces of a V row
+    constexpr int KSTEPS = KT * KV / kThreads;
+    constexpr int VSTEPS = D * VV / kThreads;
+    static_assert(KSTEPS * kThreads == KT * KV && VSTEPS * kThreads == D * VV, "tile split");
     __shared__ __align__(16) T tl;
 
     const int tid = threadIdx.x;
@@ -106,19 +115,21 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = qi < p.S ? load8(qrow + 32 * c) : 0;
     const float qs = p.q_scale[(b * p.h + j) * p.W + tile] * p.score_scale;
+    const float* ksc = p.k_scale + (b * p.h + j) * p.W;
 
     v4f o[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) o[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -__builtin_inff(), lsum = 0.0f;
 
-    const int64_t ntiles = (p.used + 63) / 64;
+    const int64_t ntiles = (p.used + KT - 1) / KT;
     const int8_t* kg = p.k8 + b * p.S * hD + j * D;
     const uint8_t* vg = p.v8 + ((b * D) * p.h + j) * p.spad;
     const int64_t vrow = p.h * p.spad;         // bytes between channel rows of v8
 
     // Coalesced tile loads into registers (rows of k8 are 16-byte pieces of D bytes; rows
-    // of the tile's v8 are 64 bytes of one channel).  K rows past `used` are zero.
+    // of the tile's v8 are KT bytes of one channel).  K rows past `used` and V columns past
+    // Spad are zero.
     uint4 kr[KSTEPS], vr[VSTEPS];
     auto fetch = [&](int64_t t0) {
 #pragma unroll
@@ -130,8 +141,10 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
         }
 #pragma unroll
         for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * kThreads + tid, d = e / 4, piece = e % 4;
-            vr[s] = *reinterpret_cast<const uint4*>(vg + d * vrow + t0 + 16 * piece);
+            const int e = s * kThreads + tid, d = e / VV, piece = e % VV;
+            const int64_t t = t0 + 16 * piece;
+            vr[s] = t < p.spad ? *reinterpret_cast<const uint4*>(vg + d * vrow + t)
+                               : make_uint4(0, 0, 0, 0);
         }
     };
     auto stash = [&](int buf) {
@@ -142,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
         }
 #pragma unroll
         for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * kThreads + tid, d = e / 4, piece = e % 4;
+            const int e = s * kThreads + tid, d = e / VV, piece = e % VV;
             *reinterpret_cast<uint4*>(&tl.v[buf][d * T::VROW + 16 * piece]) = vr[s];
         }
     };
@@ -152,14 +165,14 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
 
     for (int64_t kt = 0; kt < ntiles; ++kt) {
         const int buf = (int)(kt & 1);
-        const int64_t t0 = kt * 64;
-        if (kt + 1 < ntiles) fetch(t0 + 64);   // in flight while this tile is computed
+        const int64_t t0 = kt * KT;
+        if (kt + 1 < ntiles) fetch(t0 + KT);   // in flight while this tile is computed
         const uint8_t* kl = tl.k[buf];
         const uint8_t* vl = tl.v[buf];
         // S^T for keys t0 + 16 kb + [0, 16): lane holds keys t0 + 16 kb + 4 grp + r.
-        v4i s[4];
+        v4i s[KB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             s[kb] = v4i{0, 0, 0, 0};
             const uint8_t* krow = kl + (16 * kb + col) * T::KROW + 8 * grp;
 #pragma unroll
@@ -167,24 +180,30 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
                 s[kb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
                     *reinterpret_cast<const int64_t*>(krow + 32 * c), qf[c], s[kb], 0, 0, 0);
         }
-        const float sc = qs * p.k_scale[(b * p.h + j) * p.W + kt];
-        float x[4][4];
+        // one K scale per 64 keys; a group past the scale width holds no live key
+        float sc[KT / 64];
+#pragma unroll
+        for (int g = 0; g < KT / 64; ++g) {
+            const int64_t gi = t0 / 64 + g;
+            sc[g] = gi < p.W ? qs * ksc[gi] : 0.0f;
+        }
+        float x[KB][4];
         float tmax = -__builtin_inff();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t t = t0 + 16 * kb + 4 * grp + r;
-                x[kb][r] = t < p.used ? (float)s[kb][r] * sc : -__builtin_inff();
+                x[kb][r] = t < p.used ? (float)s[kb][r] * sc[kb / 4] : -__builtin_inff();
                 tmax = fmaxf(tmax, x[kb][r]);
             }
         tmax = quad_max(tmax);
         const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         float psum = 0.0f;
-        uint32_t pw[4];
+        uint32_t pw[KB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -196,19 +215,23 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
         psum = quad_sum(psum);
         lsum = lsum * alpha + psum;
         m = mnew;
-        // P^T fragments: keys (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp + [0, 4)),
-        // and the V^T rows (channels) in the same key order.
-        const int64_t pf0 = (int64_t)pw[0] | ((int64_t)pw[1] << 32);
-        const int64_t pf1 = (int64_t)pw[2] | ((int64_t)pw[3] << 32);
+        // P^T fragments, 32 keys each: (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp +
+        // [0, 4)); the V^T rows (channels) are read in the same key order.
+        int64_t pf[KB / 2];
+#pragma unroll
+        for (int hf = 0; hf < KB / 2; ++hf)
+            pf[hf] = (int64_t)pw[2 * hf] | ((int64_t)pw[2 * hf + 1] << 32);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const uint32_t* v32 =
                 reinterpret_cast<const uint32_t*>(vl + (16 * cb + col) * T::VROW + 4 * grp);
-            const int64_t va0 = (int64_t)v32[0] | ((int64_t)v32[4] << 32);    // keys +0, +16
-            const int64_t va1 = (int64_t)v32[8] | ((int64_t)v32[12] << 32);   // keys +32, +48
             v4f acc = o[cb] * alpha;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va0, pf0, acc, 0, 0, 0);
-            o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va1, pf1, acc, 0, 0, 0);
+#pragma unroll
+            for (int hf = 0; hf < KB / 2; ++hf) {
+                const int64_t va = (int64_t)v32[8 * hf] | ((int64_t)v32[8 * hf + 4] << 32);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pf[hf], acc, 0, 0, 0);
+            }
+            o[cb] = acc;
         }
         if (kt + 1 < ntiles) stash(buf ^ 1);   // the other buffer: nobody reads it now
         __syncthreads();
