@@ -1,0 +1,118 @@
+"""The library launches on the stream it is given and records into HIP graphs (GPU).
+
+Every entry point takes the stream as an argument, allocates nothing and never synchronizes
+the host, so the whole group pipeline can run on a side stream and can be captured once into
+a graph and replayed.  Each replay is checked against the oracle, with the program's own
+eager work and synchronizations between replays, and new inputs copied in between.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import precision_attention_input_amd as ulp
+from precision_attention_input_amd import workloads as W
+import oracle
+from oracle import pipeline
+
+from gpu_helpers import DEV, assert_bits_equal, compare_all, run_group, say, to_dev
+from helpers import small
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, d):
+    return pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                              used_sequence=w.used, scale_sequence=w.scale_sequence)
+
+
+def test_pipeline_on_a_side_stream(olib):
+    w = W.UNALIGNED_PADDED
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g = run_group(w, dd)          # every launch goes to `side`
+    side.synchronize()
+    compare_all(g, _oracle(w, d), w, "side stream")
+
+
+def _alloc(w):
+    P, L, B, H, D = w.P, w.L, w.B, w.H, w.D
+    f = dict(dtype=torch.float32, device=DEV)
+    sl = ulp.slots(L)
+    st = (torch.empty(P, B, H, sl, **f), torch.empty(P, B, H, sl, **f),
+          torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f))
+    grp = ulp.group_buffer(B, L, H, D, P, DEV)
+    out = ulp._alloc_unpack(DEV, ulp.unpack_shapes(B, L, w.h, D, P, w.scale_sequence),
+                            lead=(P,))
+    kmf = torch.empty(B, H, D, **f)
+    kmd = torch.empty(B, H, D, dtype=w.dtype, device=DEV)
+    ws = torch.empty(int(ulp.lib().ulp_k_mean_workspace_bytes(B, L, H, D, P,
+                                                               ulp._none(w.used))),
+                     dtype=torch.uint8, device=DEV)
+    return st, grp, out, (kmf, kmd), ws
+
+
+def _step(w, src, bufs):
+    """K mean -> statistics -> derive -> pack -> unpack, all on the current stream."""
+    st, grp, out, km, ws = bufs
+    P, L = w.P, w.L
+    ulp.k_mean(src["K"], world_size=P, used_sequence=w.used, workspace=ws, out=km)
+    qa, ka, qm, km_ = ulp.group_stats(src["Q"], src["K"], km[1], world_size=P,
+                                      used_sequence=w.used, out=st)
+    ulp.group_derive(qa, ka, qm, km_, km[1], local_sequence=L, world_size=P)
+    ulp.group_pack(src["Q"], src["K"], src["V"], km[1], qa, ka, world_size=P, group=grp)
+    ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
+                     world_size=P, aligned=w.aligned, scale_sequence=w.scale_sequence,
+                     out=out)
+
+
+@pytest.mark.parametrize("w", [W.TINY, small(B=2, P=4, L=100, H=8, D=128,
+                                             dtype=torch.float16, used=350,
+                                             scale_sequence=350, seed=31)],
+                         ids=["tiny", "b2_p4_l100_fp16_u350"])
+def test_pipeline_in_a_hip_graph(olib, w):
+    """Captured once, replayed on three different inputs copied into the captured buffers;
+    every replay matches the oracle run on the same inputs (the mean included: it is formed
+    inside the graph by ulp_k_mean and compared with the oracle's)."""
+    inputs = [W.generate(w.with_(seed=w.seed + 100 * i)) for i in range(3)]
+    src = {n: torch.empty_like(W.stacked_shards(inputs[0][n], w.P), device=DEV)
+           for n in ("Q", "K", "V")}
+    bufs = _alloc(w)
+
+    def load(d):
+        for n in ("Q", "K", "V"):
+            src[n].copy_(W.stacked_shards(d[n], w.P).to(DEV))
+
+    load(inputs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):            # warm-up outside the capture
+        _step(w, src, bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _step(w, src, bufs)
+    torch.cuda.synchronize()
+    for i, d in enumerate(inputs):
+        load(d)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[graph] {w.name} replay {i}")
+        st, grp, out, km, ws = bufs
+        # the mean formed inside the graph: the oracle's within its tolerance, and the
+        # input of the oracle run below (k_mean_global is an input of the path)
+        mf, md = km[0].cpu(), km[1].cpu()
+        of, _ = oracle.k_mean(W.stacked_shards(d["K"], w.P), used_sequence=w.used)
+        assert torch.allclose(mf, of, rtol=1e-6, atol=1e-6), f"replay {i}: K mean"
+        assert_bits_equal(md, mf.to(w.dtype), f"replay {i}: dtype mean = RNE(fp32 mean)")
+        ref = _oracle(w, dict(d, mean=md))
+        for p in range(w.P):
+            for k, name in enumerate(("q8", "k8", "v8", "q_scale", "k_scale")):
+                assert_bits_equal(out[k][p], ref["outs"][p][k], f"replay {i}: {name} dest {p}")
+        # eager work between replays must not disturb the graph's buffers
+        _ = (src["Q"].float() * 2).sum().item()
