@@ -311,3 +311,38 @@ def test_invalid_arguments_launch_nothing(olib):
         ulp.k_grouped_amax(dd["K"][0], dd["mean"], rank=2, world_size=2, out=out)
     torch.cuda.synchronize()
     assert (out == 0).all() and _margins_ok(buf)
+
+
+# ----------------------------------------------------------------- seeded random shapes
+
+def _random_cases(n=24, seed=2024):
+    g = torch.Generator().manual_seed(seed)
+    cases = []
+    for i in range(n):
+        P = [2, 4, 6, 8][int(torch.randint(0, 4, (1,), generator=g))]
+        L = int(torch.randint(1, 300, (1,), generator=g))
+        h = int(torch.randint(1, 4, (1,), generator=g))
+        B = int(torch.randint(1, 3, (1,), generator=g))
+        D = [64, 128][int(torch.randint(0, 2, (1,), generator=g))]
+        dtype = [torch.bfloat16, torch.float16][int(torch.randint(0, 2, (1,), generator=g))]
+        S = P * L
+        used = int(torch.randint(1, S + 1, (1,), generator=g))
+        used = None if (i % 4 == 0 or used == S) else used
+        ss = None if i % 3 else (used or S)
+        cases.append(small(B=B, P=P, L=L, H=P * h, D=D, dtype=dtype, used=used,
+                           scale_sequence=ss, seed=7000 + i))
+    return cases
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("w", RANDOM, ids=[f"{w.name}_u{w.used}_s{w.scale_sequence}"
+                                            for w in RANDOM])
+def test_random_shapes(olib, w):
+    """Seeded random geometry (world size, shard length, heads, batch, head_dim, dtype, live
+    prefix, consumer width) through the group launches, every byte against the oracle."""
+    say(f"[random] {w.name} used={w.used} ss={w.scale_sequence}")
+    d = W.generate(w)
+    dd = to_dev(d, w.P)
+    compare_all(run_group(w, dd), oracle_run(w, d), w, "random")
