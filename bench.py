@@ -347,6 +347,27 @@ def main():
         k_mean(sets[i % nsets])
     k_mean_ms = timed(k_mean, K)
 
+    # Statistics together with the K mean: the mean then the statistics (two reads of K),
+    # and the one-read entry point that forms both from one pass over K.
+    ws2 = torch.empty(int(ulp.lib().ulp_group_stats_with_mean_workspace_bytes(B, L, H, D, P)),
+                      dtype=torch.uint8, device=dev)
+    sm_out = tuple(t.clone() for t in sets[0]["stats"]) + km_out
+
+    def stats_mean_separate(s):
+        k_mean(s)
+        ulp.group_stats(s["Q"], s["K"], km_out[1], world_size=P, used_sequence=w.used,
+                        out=s["stats"])
+
+    def stats_mean_one_read(s):
+        ulp.group_stats_with_mean(s["Q"], s["K"], world_size=P, used_sequence=w.used,
+                                  workspace=ws2, out=sm_out)
+
+    for i in range(args.warmup):
+        stats_mean_separate(sets[i % nsets])
+        stats_mean_one_read(sets[i % nsets])
+    sm_sep_ms = timed(stats_mean_separate, K)
+    sm_one_ms = timed(stats_mean_one_read, K)
+
     pu_bytes = nb["pack"] + nb["unpack"]
     value = pu_bytes / (pu_ms * 1e-3) / 1e9
     pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
@@ -388,6 +409,8 @@ def main():
         "amax_gbps": round(nb["stats"] / (stats_ms * 1e-3) / 1e9, 2),
         "k_mean_ms": round(k_mean_ms, 5),
         "k_mean_gbps": round(nb["k_mean"] / (k_mean_ms * 1e-3) / 1e9, 2),
+        "stats_with_mean_ms": {"k_mean_then_stats": round(sm_sep_ms, 5),
+                               "one_read_of_k": round(sm_one_ms, 5)},
         "step_ms_events": round(step_ms, 5),
         "step_gbps": round((pu_bytes + nb["stats"]) / (step_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),

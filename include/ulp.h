@@ -220,6 +220,30 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
                float* mean_f32, void* mean_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * Statistics of every rank together with the global K mean, reading Q and K once each.
+ * The centered amax of k_grouped_amax (description) needs k_mean_global (Parameters), and
+ * forming that mean is itself a pass over K; here one pass over K records, per (rank, b,
+ * head, slot, channel), the raw min / max over the rows the amax runs on and the binary64
+ * sum over live rows.  The mean follows from the sums (same definition as ulp_k_mean) and
+ * every slot's amax from max_d max(RN(max - m), RN(m - min)) with m the dtype mean, the
+ * identity derive_k_boundary_amax (description) rests on: outputs are bit-identical to
+ * ulp_group_stats run with this mean.
+ *   q, k        stacked [P, B, L, H, D] dtype.
+ *   workspace   device memory of ulp_group_stats_with_mean_workspace_bytes() bytes, 8-byte
+ *               aligned at least, owned by the caller; contents on entry do not matter.
+ *   q_amax, k_amax      [P, B, H, slots(L)] float;  q_minmax, k_minmax [P, B, H, 2, 2, D].
+ *   k_mean_f32  [B, H, D] float;  k_mean_dtype [B, H, D] dtype (the k_mean_global to pass
+ *               on to derive and pack).
+ * --------------------------------------------------------------------------------- */
+int64_t ulp_group_stats_with_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D,
+                                                  int world_size);
+int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B, int64_t L,
+                              int64_t H, int64_t D, int world_size, int64_t used_sequence,
+                              void* workspace, int64_t workspace_bytes, float* q_amax,
+                              float* k_amax, float* q_minmax, float* k_minmax,
+                              float* k_mean_f32, void* k_mean_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * Consumer check (not a step of the pack/unpack path).  Attention over one destination's
  * unpacked tensors, read the way the Sage consumer named by unpack_for_sage (description,
  * Returns) reads them: for rows i, t < used,

@@ -22,7 +22,7 @@ __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
     "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
-    "consumer_attention",
+    "group_stats_with_mean", "consumer_attention",
     "unpack_shapes",
 ]
 
@@ -71,6 +71,9 @@ def lib():
                                  i32),
             "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
             "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
+            "ulp_group_stats_with_mean_workspace_bytes": ([i64, i64, i64, i64, i32], i64),
+            "ulp_group_stats_with_mean": ([vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, i64,
+                                           vp, vp, vp, vp, vp, vp, vp], i32),
             "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                         vp, vp], i32),
         }
@@ -312,6 +315,28 @@ def k_mean(k, *, world_size, used_sequence=None, workspace=None, out=None):
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _p(mf), _p(md), _stream(k)))
     return mf, md
+
+
+def group_stats_with_mean(q, k, *, world_size, used_sequence=None, workspace=None, out=None):
+    """Stacked shards [P,B,L,H,D] -> (q_amax, k_amax, q_minmax, k_minmax, k_mean_f32,
+    k_mean_dtype), reading Q and K once each: the statistics of ``group_stats`` with the
+    global K mean formed in the same pass over K."""
+    P, B, L, H, D = q.shape
+    need = int(lib().ulp_group_stats_with_mean_workspace_bytes(B, L, H, D, world_size))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        f = dict(dtype=torch.float32, device=q.device)
+        out = (torch.empty(P, B, H, slots(L), **f), torch.empty(P, B, H, slots(L), **f),
+               torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f),
+               torch.empty(B, H, D, **f), torch.empty(B, H, D, dtype=q.dtype, device=q.device))
+    _dev(q, k, workspace, *out)
+    qa, ka, qm, km, mf, md = out
+    _check(lib().ulp_group_stats_with_mean(
+        _p(q), _p(k), _dt(q), B, L, H, D, world_size, _none(used_sequence), _p(workspace),
+        workspace.numel() * workspace.element_size(), _p(qa), _p(ka), _p(qm), _p(km), _p(mf),
+        _p(md), _stream(q)))
+    return tuple(out)
 
 
 # ------------------------------------------------------------------------- consumer check

@@ -387,6 +387,66 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
     return launched(ulp::launch_kmean(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int64_t ulp_group_stats_with_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D,
+                                                  int world_size) {
+    if (B < 1 || L < 1 || H < 1 || D < 1 || world_size < 1) return 0;
+    return ulp::kstats_workspace_bytes(B, L, H, D, world_size);
+}
+
+int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B, int64_t L,
+                              int64_t H, int64_t D, int world_size, int64_t used_sequence,
+                              void* workspace, int64_t workspace_bytes, float* q_amax,
+                              float* k_amax, float* q_minmax, float* k_minmax,
+                              float* k_mean_f32, void* k_mean_dtype, void* stream) {
+    const char* fn = "ulp_group_stats_with_mean";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "q", q));
+    TRY(check_ptr(fn, "k", k));
+    TRY(check_ptr(fn, "workspace", workspace));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    TRY(check_ptr(fn, "q_minmax", q_minmax));
+    TRY(check_ptr(fn, "k_minmax", k_minmax));
+    TRY(check_ptr(fn, "k_mean_f32", k_mean_f32));
+    TRY(check_ptr(fn, "k_mean_dtype", k_mean_dtype));
+    const int64_t need = ulp::kstats_workspace_bytes(B, L, H, D, world_size);
+    if (workspace_bytes < need)
+        return fail(ULP_EINVAL, "%s: workspace of %lld bytes, %lld needed", fn,
+                    (long long)workspace_bytes, (long long)need);
+    if (B * H * D / 64 >= kMaxGrid || (int64_t)world_size * B * H * ulp::slots_of(L) / 4 >= kMaxGrid)
+        return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
+    const int64_t S = world_size * L;
+    // Q: grouped amax of raw values and boundary min/max, as ulp_group_stats does
+    ulp::StatsLaunch qa{};
+    qa.x[0] = static_cast<const uint16_t*>(q);
+    qa.amax[0] = q_amax;
+    qa.minmax[0] = q_minmax;
+    qa.x_rank_stride = B * L * H * D;
+    qa.amax_rank_stride = B * H * ulp::slots_of(L);
+    qa.minmax_rank_stride = B * H * 4 * D;
+    qa.B = B; qa.L = L; qa.H = H; qa.D = D; qa.P = world_size;
+    qa.used = used_or_s(used_sequence, S);
+    qa.rank0 = 0; qa.nranks = world_size; qa.dtype = dtype;
+    const int rc = launched(ulp::launch_stats(qa, static_cast<hipStream_t>(stream)), fn);
+    if (rc != ULP_OK) return rc;
+    // K: one pass for the per-group min/max, the boundary min/max and the sums; then the
+    // mean and the grouped amax
+    ulp::KStatsLaunch ka{};
+    ka.k = static_cast<const uint16_t*>(k);
+    char* ws = static_cast<char*>(workspace);
+    ka.mm = reinterpret_cast<float*>(ws);
+    ka.sum = reinterpret_cast<double*>(ws + world_size * B * H * ulp::slots_of(L) * D * 8);
+    ka.minmax = k_minmax;
+    ka.amax = k_amax;
+    ka.mean_f32 = k_mean_f32;
+    ka.mean_dtype = static_cast<uint16_t*>(k_mean_dtype);
+    ka.B = B; ka.L = L; ka.H = H; ka.D = D; ka.P = world_size;
+    ka.used = used_or_s(used_sequence, S);
+    ka.dtype = dtype;
+    return launched(ulp::launch_kstats(ka, static_cast<hipStream_t>(stream)), fn);
+}
+
 int ulp_consumer_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                            const float* q_scale, const float* k_scale, const float* v_scale,
                            int64_t B, int64_t S, int64_t h, int64_t D, int64_t W,

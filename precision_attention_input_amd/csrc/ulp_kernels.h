@@ -60,6 +60,19 @@ struct KMeanLaunch {
     int dtype;
 };
 
+// K statistics and the K mean from one read of the stacked K shards.
+struct KStatsLaunch {
+    const uint16_t* k;        // [P, B, L, H, D]
+    float* mm;                // workspace [P, B, H, slots, 2, D]
+    double* sum;              // workspace [P, B, H, slots, D]
+    float* minmax;            // [P, B, H, 2, 2, D]
+    float* amax;              // [P, B, H, slots]
+    float* mean_f32;          // [B, H, D]
+    uint16_t* mean_dtype;     // [B, H, D]
+    int64_t B, L, H, D, P, used;
+    int dtype;
+};
+
 // Attention over one destination's unpacked tensors (the consumer check).
 struct ConsumerLaunch {
     const int8_t *q8, *k8;         // [B, S, h, D]
@@ -77,6 +90,7 @@ int64_t kmean_chunks(int64_t B, int64_t H, int64_t D, int64_t used);
 hipError_t launch_stats(const StatsLaunch& a, hipStream_t stream);
 hipError_t launch_kmean(const KMeanLaunch& a, hipStream_t stream);
 hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream);
+hipError_t launch_kstats(const KStatsLaunch& a, hipStream_t stream);
 hipError_t launch_derive(const DeriveLaunch& a, hipStream_t stream);
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream);
@@ -89,6 +103,11 @@ inline int64_t chunk_section(int64_t B, int64_t L, int64_t h, int64_t D) {
 }
 inline int64_t chunk_scale_section(int64_t B, int64_t L, int64_t h) {
     return align256(4 * B * h * slots_of(L));
+}
+// workspace of the one-read K statistics: raw min / max (fp32) and sums (fp64) per
+// (rank, b, head, slot, channel)
+inline int64_t kstats_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D, int64_t P) {
+    return P * B * H * slots_of(L) * D * (2 * 4 + 8);
 }
 inline int64_t chunk_bytes_of(int64_t B, int64_t L, int64_t h, int64_t D) {
     return 3 * chunk_section(B, L, h, D) + 2 * chunk_scale_section(B, L, h);

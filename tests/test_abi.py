@@ -177,3 +177,17 @@ def test_consumer_validation(L):
     assert call(h=0) == EINVAL
     assert call(v=A + 4) == EALIGN
     assert L.ulp_consumer_attention(A, 0, A, A, A, None, 1, 128, 2, 64, 2, 128, A, None) == EINVAL
+
+
+def test_stats_with_mean_validation(L):
+    need = L.ulp_group_stats_with_mean_workspace_bytes(1, 128, 4, 64, 2)
+    assert need == 2 * 1 * 4 * 2 * 64 * 16          # P*B*H*slots*D*(2*4 + 8)
+
+    def call(dtype=0, B=1, Lq=128, H=4, D=64, P=2, used=NONE, ws=A, wsb=need, md=A):
+        return L.ulp_group_stats_with_mean(A, A, dtype, B, Lq, H, D, P, used, ws, wsb, A, A,
+                                           A, A, A, md, None)
+    assert call(wsb=need - 1) == EINVAL and b"workspace" in L.ulp_last_error()
+    assert call(md=0) == EINVAL
+    assert call(D=96) == EUNSUPPORTED
+    assert call(used=300) == EINVAL
+    assert call(ws=A + 8) == EALIGN

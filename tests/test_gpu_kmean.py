@@ -155,3 +155,49 @@ def test_k_mean_feeds_the_pipeline(olib):
     ref = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
                              used_sequence=w.used, scale_sequence=w.scale_sequence)
     compare_all(run_group(w, dd), ref, w, "pipeline with the GPU mean")
+
+
+# ----------------------------------------------------------------- statistics with the mean
+
+def _check_with_mean(w, Ks_dev, Qs_dev, label, oracle_ranks=True):
+    """group_stats_with_mean against (a) the oracle's mean within its tolerance and (b) the
+    oracle's statistics run with the GPU's dtype mean, bit for bit, and (c) ulp_group_stats
+    fed the same mean."""
+    P = w.P
+    qa, ka, qm, km, mf, md = ulp.group_stats_with_mean(Qs_dev, Ks_dev, world_size=P,
+                                                       used_sequence=w.used)
+    ra = ulp.group_stats(Qs_dev, Ks_dev, md, world_size=P, used_sequence=w.used)
+    torch.cuda.synchronize()
+    for got, ref, name in zip((qa, ka, qm, km), ra, ("q_amax", "k_amax", "q_minmax",
+                                                     "k_minmax")):
+        assert_bits_equal(got, ref, f"{label}: {name} vs group_stats with the same mean")
+    Ks = Ks_dev.cpu()
+    of, _ = oracle.k_mean(Ks, used_sequence=w.used)
+    tol = REL * torch.maximum(of.abs(), channel_scale(Ks, w.used or w.S))
+    assert bool(((mf.cpu().double() - of.double()).abs() <= tol.double()).all()), label
+    assert_bits_equal(md, mf.cpu().to(Ks.dtype), f"{label}: dtype mean = RNE(fp32 mean)")
+    if oracle_ranks:
+        mdc = md.cpu()
+        for r in range(P):
+            kw = dict(rank=r, world_size=P, used_sequence=w.used)
+            assert_bits_equal(ka[r], oracle.k_grouped_amax(Ks[r], mdc, **kw), f"{label} k_amax r{r}")
+            assert_bits_equal(km[r], oracle.boundary_minmax(Ks[r], **kw), f"{label} k_minmax r{r}")
+    say(f"[stats+mean] {label}: ok")
+
+
+@pytest.mark.parametrize("wname", [w.name for w in W.WORKLOADS])
+def test_stats_with_mean_workloads(olib, wname):
+    w = W.BY_NAME[wname]
+    d = W.generate(w)
+    Ks = W.stacked_shards(d["K"], w.P).to(DEV)
+    Qs = W.stacked_shards(d["Q"], w.P).to(DEV)
+    del d
+    _check_with_mean(w, Ks, Qs, wname, oracle_ranks=w.S <= 10000)
+
+
+@pytest.mark.parametrize("w,used", EDGE, ids=[f"{w.name}_u{u}" for w, u in EDGE])
+def test_stats_with_mean_edges(olib, w, used):
+    w = w.with_(used=used)
+    d = W.generate(w)
+    _check_with_mean(w, W.stacked_shards(d["K"], w.P).to(DEV),
+                     W.stacked_shards(d["Q"], w.P).to(DEV), f"{w.name} used={used}")
