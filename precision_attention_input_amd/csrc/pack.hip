@@ -12,13 +12,14 @@
 //
 // Work decomposition: the shard is a [B*L, H*D/16] array of 16-element vectors; one thread
 // owns one vector of each of Q, K and V.  It issues all of its loads first (amax of both
-// tensors, the K mean, 2 x 16 bytes of each of Q, K, V), runs the quantization fast path of
-// all three tensors as straight-line code, stores three 16-byte code vectors, and only then
-// takes the rare exact-quotient fix-up (the near-half-integer test above), which rewrites
-// the 16 codes it affects.  The kernel is VALU-bound, so the per-thread overhead is kept
-// small: 32-bit column arithmetic, one IEEE division and one v_rcp_f32 per tensor.  A
-// 256-thread workgroup covers kRows rows x kCols vectors, so every wave reads and writes
-// whole 1 KB row segments; the grid is (B x row blocks, column blocks, ranks).
+// tensors, the K mean, 2 x 16 bytes of each of Q, K, V), then quantizes: centered K and bf16
+// Q by the division-free exact decision (quantize_exact in ulp_device.h), fp16 Q by the
+// reciprocal fast path with the exact decision as a per-wave fallback when a quotient lies
+// near a half-integer; V by the E4M3 conversion.  The kernel is VALU-bound on bf16 data, so
+// the per-thread overhead is kept small: 32-bit column arithmetic, one IEEE division and one
+// v_rcp_f32 per tensor.  A 256-thread workgroup covers kRows rows x kCols vectors, so every
+// wave reads and writes whole 1 KB row segments; the grid is (B x row blocks, column
+// blocks, ranks).
 #include "ulp_device.h"
 #include "ulp_kernels.h"
 
