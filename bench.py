@@ -58,10 +58,16 @@ def algorithmic_bytes(w, v_scale: bool = False) -> dict:
 
 
 def kernel_hash() -> str:
+    """Hash of the pack kernel's source with comments and whitespace removed, so that the
+    recorded traffic stays attached to the code it was measured on, not to its comments."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
