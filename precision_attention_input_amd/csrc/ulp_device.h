@@ -93,21 +93,62 @@ __device__ __forceinline__ float clampf(float x, float lo, float hi) {
     return __builtin_amdgcn_fmed3f(x, lo, hi);
 }
 
-// Max over the lanes of a wave that differ only in the bits of `mask_bits` (xor tree).
-template <int OFFSETS_MASK>
-__device__ __forceinline__ float wave_max_xor(float v) {
+// Max / min over the lanes of a wave that differ only in the bits of OFFSETS_MASK, left in
+// every such lane.  No LDS traffic: inside a 16-lane row the lanes are combined with DPP
+// (row_mirror pairs lane i with 15 - i, row_half_mirror i with 7 - i inside each 8, then the
+// quad permutations [2,3,0,1] and [1,0,3,2]: after these every lane has met its whole row,
+// or its whole half-row when only bits 0-2 are asked for); bits 4 and 5 use gfx950's
+// v_permlane16_swap / v_permlane32_swap on two copies of the value.  Other bit patterns
+// fall back to LDS lane permutes.  Max and min are order-independent, so every lane ends
+// with the same bits.
+template <bool MAX>
+__device__ __forceinline__ float pick(float a, float b) {
+    return MAX ? fmaxf(a, b) : fminf(a, b);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <bool MAX, int OFFSETS_MASK>
+__device__ __forceinline__ float wave_reduce_xor(float v) {
+    constexpr int low = OFFSETS_MASK & 15;
+    if constexpr (low == 15) {
+        v = pick<MAX>(v, dpp<0x140>(v));        // row_mirror
+        v = pick<MAX>(v, dpp<0x141>(v));        // row_half_mirror
+        v = pick<MAX>(v, dpp<0x4E>(v));         // quad_perm [2,3,0,1]
+        v = pick<MAX>(v, dpp<0xB1>(v));         // quad_perm [1,0,3,2]
+    } else if constexpr (low == 7) {
+        v = pick<MAX>(v, dpp<0x141>(v));
+        v = pick<MAX>(v, dpp<0x4E>(v));
+        v = pick<MAX>(v, dpp<0xB1>(v));
+    } else {
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-        if (OFFSETS_MASK & off) v = fmaxf(v, __shfl_xor(v, off, 64));
+        for (int off = 1; off < 16; off <<= 1)
+            if (low & off) v = pick<MAX>(v, __shfl_xor(v, off, 64));
+    }
+    if constexpr ((OFFSETS_MASK & 16) != 0) {
+        const unsigned u = __float_as_uint(v);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = pick<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr ((OFFSETS_MASK & 32) != 0) {
+        const unsigned u = __float_as_uint(v);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = pick<MAX>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     return v;
 }
 
 template <int OFFSETS_MASK>
+__device__ __forceinline__ float wave_max_xor(float v) {
+    return wave_reduce_xor<true, OFFSETS_MASK>(v);
+}
+
+template <int OFFSETS_MASK>
 __device__ __forceinline__ float wave_min_xor(float v) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1)
-        if (OFFSETS_MASK & off) v = fminf(v, __shfl_xor(v, off, 64));
-    return v;
+    return wave_reduce_xor<false, OFFSETS_MASK>(v);
 }
 
 // ---------------------------------------------------------------- INT8 quantization
