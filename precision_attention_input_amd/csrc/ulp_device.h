@@ -97,7 +97,8 @@ __device__ __forceinline__ float clampf(float x, float lo, float hi) {
 // every such lane.  No LDS traffic: inside a 16-lane row the lanes are combined with DPP
 // (row_mirror pairs lane i with 15 - i, row_half_mirror i with 7 - i inside each 8, then the
 // quad permutations [2,3,0,1] and [1,0,3,2]: after these every lane has met its whole row,
-// or its whole half-row when only bits 0-2 are asked for); bits 4 and 5 use gfx950's
+// or its whole half-row when only bits 0-2 are asked for; bit 3 alone is a rotation of the
+// row by 8); bits 4 and 5 use gfx950's
 // v_permlane16_swap / v_permlane32_swap on two copies of the value.  Other bit patterns
 // fall back to LDS lane permutes.  Max and min are order-independent, so every lane ends
 // with the same bits.
@@ -123,6 +124,8 @@ __device__ __forceinline__ float wave_reduce_xor(float v) {
         v = pick<MAX>(v, dpp<0x141>(v));
         v = pick<MAX>(v, dpp<0x4E>(v));
         v = pick<MAX>(v, dpp<0xB1>(v));
+    } else if constexpr (low == 8) {
+        v = pick<MAX>(v, dpp<0x128>(v));        // row_ror 8: lane i meets lane i ^ 8
     } else {
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1)
