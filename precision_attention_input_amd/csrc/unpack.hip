@@ -10,9 +10,10 @@
 //            it is a plain 16-byte vector copy (2 or 8 vectors per thread per workgroup);
 //   * V:     each wave transposes a 16-row x 16-byte register block per lane: 16 coalesced
 //            16-byte loads along channels, 16 byte-level 4x4 transposes with v_perm_b32,
-//            16 coalesced 16-byte stores along time.  A wave covers 128 (D = 128) or 256
-//            (D = 64) time steps x all D channels of one (b, head); rows are fetched from
-//            whichever source holds them, so tiles that straddle shards need no special case;
+//            16 coalesced 16-byte stores along time.  A wave covers 128 time steps x 128
+//            bytes of each row (one head at D = 128, two neighbouring heads at D = 64, so
+//            loads are whole cache lines); rows are fetched from whichever source holds
+//            them, so tiles that straddle shards need no special case;
 //   * scales: group g's scale is read from the source holding its first row, floor(64g/L).
 #include "ulp_device.h"
 #include "ulp_kernels.h"
@@ -30,9 +31,6 @@ namespace {
 #endif
 constexpr int kUnrollSmall = ULP_UNPACK_UNROLL_SMALL;
 constexpr int kUnrollLarge = ULP_UNPACK_UNROLL_LARGE;
-#ifndef ULP_UNPACK_V_ORDER
-#define ULP_UNPACK_V_ORDER 0
-#endif
 
 struct UnpackParams {
     const uint8_t* recv;
@@ -83,31 +81,23 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
     bid -= p.n_copy;
 
     if (bid < p.n_v) {
-        constexpr int DB = D / 16;             // 16-byte channel blocks per row
-        constexpr int T = 16 * (64 / DB);      // time steps per wave tile
+        // Every wave covers 128 bytes of each received row, all channels of one head
+        // (D = 128) or of two neighbouring heads (D = 64), so every load is whole 128-byte
+        // lines, and 128 time steps: lane (db, tb) holds rows t0 + [0, 16) of channel
+        // block db.
+        constexpr int HPW = 128 / D;           // heads per wave
+        constexpr int T = 128;                 // time steps per wave tile
         const int wave = tid >> 6, lane = tid & 63;
-#if ULP_UNPACK_V_ORDER == 0
-        const int64_t item = bid * 4 + wave;   // (b, head, tile)
-        if (item >= p.B * h * p.v_tiles) return;
+        const int64_t hw = (h + HPW - 1) / HPW;
+        const int64_t item = bid * 4 + wave;   // (b, head group, tile)
+        if (item >= p.B * hw * p.v_tiles) return;
         const int64_t tile = item % p.v_tiles, bj = item / p.v_tiles;
-        const int64_t j = bj % h, b = bj / h;
-#elif ULP_UNPACK_V_ORDER == 1
-        const int64_t item = bid * 4 + wave;   // (b, tile, head)
-        if (item >= p.B * h * p.v_tiles) return;
-        const int64_t j = item % h, bt = item / h;
-        const int64_t tile = bt % p.v_tiles, b = bt / p.v_tiles;
-#else
-        // workgroup = 4 consecutive tiles of one head; consecutive workgroups = the heads of
-        // the same rows
-        const int64_t ntg = (p.v_tiles + 3) / 4;
-        const int64_t j = bid % h, btg = bid / h;
-        const int64_t tile = (btg % ntg) * 4 + wave, b = btg / ntg;
-        if (tile >= p.v_tiles) return;
-#endif
-        const int db = lane % DB, tb = lane / DB;
+        const int64_t jw = bj % hw, b = bj / hw;
+        const int db = lane & 7, tb = lane >> 3;
+        const int64_t j = jw * HPW + db / (D / 16);
         const int64_t t0 = tile * T + tb * 16;
-        if (t0 >= p.spad) return;
-        const int d0 = db * 16;
+        if (t0 >= p.spad || j >= h) return;
+        const int d0 = (db % (D / 16)) * 16;
 
         uint32_t w[16][4];
         int64_t s = t0 / L, l = t0 % L;
@@ -171,13 +161,9 @@ UnpackGeometry unpack_geometry(int64_t B, int64_t L, int64_t h, int64_t D, int64
     g.n_copy = 2 * P * B * g.copy_bps;
     const int64_t S = P * L;
     g.spad = (S + kGroup - 1) / kGroup * kGroup;
-    const int64_t T = 16 * (64 / (D / 16));
-    g.v_tiles = (g.spad + T - 1) / T;
-#if ULP_UNPACK_V_ORDER == 2
-    g.n_v = B * h * ((g.v_tiles + 3) / 4);
-#else
-    g.n_v = (B * h * g.v_tiles + 3) / 4;
-#endif
+    const int64_t hw = (h + 128 / D - 1) / (128 / D);   // head groups of 128 bytes
+    g.v_tiles = (g.spad + 127) / 128;
+    g.n_v = (B * hw * g.v_tiles + 3) / 4;
     g.n_scale = (B * h * W + kThreads - 1) / kThreads;
     return g;
 }
