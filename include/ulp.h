@@ -28,6 +28,8 @@
  *    ulp_last_error() then describes the problem.  ULP_ELAUNCH reports a HIP launch error.
  *  - Zero-filling of rows >= used_sequence in Q, K and V is a caller contract
  *    (k_grouped_amax, used_sequence parameter); it is not checked.
+ *  - Q and K hold finite values.  The statistics order raw 16-bit patterns, so a NaN in
+ *    a group gives that group an unspecified amax and min/max (not an error).
  *
  * Layouts (G = 64-row group size):
  *  slots(L)      = L/64 if 64 divides L, else ceil(L/64) + 1: the most global groups an

@@ -9,18 +9,17 @@
 //
 // One 256-thread workgroup handles one (rank, tensor, b, slot, head block): at most 64 rows
 // x (256 / D) heads, i.e. 32 sixteen-byte vectors per row and 8 rows in flight, each thread
-// issuing its (up to) 8 loads before reducing.  Both statistics come out of the same pass,
-// so the fused group entry point reads Q and K exactly once.
+// issuing its (up to) 8 loads before reducing.  Per channel a thread keeps only the raw
+// extremes of its rows (three packed 16-bit integer operations per two values, Order16);
+// the amax then follows from them by the identity that derive_k_boundary_amax
+// (description) rests on, max |RN(x - m)| = max(RN(max x - m), RN(m - min x)), so the
+// per-element work is the same for the amax and the min/max, and both come out of the
+// same pass: the fused group entry point reads Q and K exactly once.
 #include "ulp_device.h"
 #include "ulp_kernels.h"
 
 namespace ulp {
 namespace {
-
-#ifndef ULP_STATS_ROWS_IN_FLIGHT
-#define ULP_STATS_ROWS_IN_FLIGHT 8
-#endif
-constexpr int kRowsInFlight = ULP_STATS_ROWS_IN_FLIGHT;
 
 struct StatsParams {
     const uint16_t* x[2];
@@ -73,55 +72,59 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
     const int64_t g = g0 + j;
     const int64_t lo = max((int64_t)kGroup * g, rank * L);
     const int64_t hi = min((int64_t)kGroup * g + kGroup, rank * L + L);
+    // Rows of the amax: [lo, amax_hi).  Rows of the min/max: [lo, min(hi, used)), which is
+    // either the same range or empty (a group wholly in the zero tail), so one pass over
+    // the amax rows serves both.
     const int64_t amax_hi =
         (p.used < p.S && g == (p.used - 1) / kGroup) ? min(hi, p.used) : hi;
-    const int64_t mm_hi = min(hi, p.used);
+    const int nrow = (int)(amax_hi - lo);           // may be <= 0
+    const bool mm_live = min(hi, p.used) > lo;
     const bool want_amax = amax_out != nullptr;
     const bool want_mm = mm_out != nullptr && (j == 0 || j == n - 1);
 
-    float m[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+    uint4 mraw = make_uint4(0, 0, 0, 0);
     if (p.mean[tensor] != nullptr && valid)
-        decode8<DT>(load16(p.mean[tensor] + (b * H + head) * D + dv * 8), m);
+        mraw = load16(p.mean[tensor] + (b * H + head) * D + dv * 8);
 
-    const uint16_t* xb = x + blockIdx.z * p.x_rank_stride + (b * L * H + head) * D + dv * 8;
+    // Raw order statistics of this thread's rows lo + rl + 8i, i < 8, per channel: no
+    // conversion or subtraction per element (the amax follows from the extremes below).
+    // Rows past the range are replaced by its last row, which leaves every extreme as it
+    // is and keeps the loop free of per-row branches.
+    const uint16_t* xr =
+        x + blockIdx.z * p.x_rank_stride + ((b * L + lo - rank * L) * H + head) * D + dv * 8;
+    const bool mine = valid && rl < nrow;           // this thread has at least one row
+    Order16 ord[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ord[w].reset();
+    if (mine) {
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = load16<NT>(xr + (int64_t)min(rl + 8 * i, nrow - 1) * H * D);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ord[0].add(v[i].x);
+            ord[1].add(v[i].y);
+            ord[2].add(v[i].z);
+            ord[3].add(v[i].w);
+        }
+    }
+
+    // Per channel: the extremes as binary32 (zeros canonicalised to +0), then
+    //   max over rows of |RN(x - m)| = max(RN(max x - m), RN(m - min x))
+    // because RN(. - m) is non-decreasing and RN(-z) = -RN(z).
+    float mn[8], mx[8], m[8];
+    decode8<DT>(mraw, m);
+    decode8<DT>(make_uint4(ord[0].min_bits(), ord[1].min_bits(), ord[2].min_bits(),
+                           ord[3].min_bits()), mn);
+    decode8<DT>(make_uint4(ord[0].max_bits(), ord[1].max_bits(), ord[2].max_bits(),
+                           ord[3].max_bits()), mx);
     float acc = -__builtin_inff();
-    float mn[8], mx[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        mn[e] = __builtin_inff();
-        mx[e] = -__builtin_inff();
-    }
-    // 8 rows per thread, kRowsInFlight loads issued before each reduction batch
-#pragma unroll
-    for (int i0 = 0; i0 < 8; i0 += kRowsInFlight) {
-        uint4 v[kRowsInFlight];
-#pragma unroll
-        for (int i = 0; i < kRowsInFlight; ++i) {
-            const int64_t s = lo + rl + 8 * (i0 + i);
-            v[i] = (valid && s < hi) ? load16<NT>(xb + (s - rank * L) * H * D)
-                                     : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < kRowsInFlight; ++i) {
-            const int64_t s = lo + rl + 8 * (i0 + i);
-            if (!(valid && s < hi)) continue;
-            float f[8];
-            decode8<DT>(v[i], f);
-            if (want_amax && s < amax_hi) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaxf(acc, __builtin_fabsf(f[e] - m[e]));
-            }
-            if (want_mm && s < mm_hi) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float cv = f[e] + 0.0f;   // -0 -> +0, every other value unchanged
-                    mn[e] = fminf(mn[e], cv);
-                    mx[e] = fmaxf(mx[e], cv);
-                }
-            }
-        }
+        mn[e] = mine ? mn[e] + 0.0f : __builtin_inff();     // -0 -> +0
+        mx[e] = mine ? mx[e] + 0.0f : -__builtin_inff();
+        acc = fmaxf(acc, fmaxf(mx[e] - m[e], m[e] - mn[e]));
     }
 
     __shared__ float red_amax[4][HB];
@@ -157,10 +160,12 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsParams p) {
         float rmn[8], rmx[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            rmn[e] = fminf(fminf(red_mn[0][c][e], red_mn[1][c][e]),
-                           fminf(red_mn[2][c][e], red_mn[3][c][e]));
-            rmx[e] = fmaxf(fmaxf(red_mx[0][c][e], red_mx[1][c][e]),
-                           fmaxf(red_mx[2][c][e], red_mx[3][c][e]));
+            rmn[e] = mm_live ? fminf(fminf(red_mn[0][c][e], red_mn[1][c][e]),
+                                     fminf(red_mn[2][c][e], red_mn[3][c][e]))
+                             : __builtin_inff();
+            rmx[e] = mm_live ? fmaxf(fmaxf(red_mx[0][c][e], red_mx[1][c][e]),
+                                     fmaxf(red_mx[2][c][e], red_mx[3][c][e]))
+                             : -__builtin_inff();
         }
         for (int e2 = 0; e2 < 2; ++e2) {
             if ((e2 == 0 && j != 0) || (e2 == 1 && j != n - 1)) continue;
