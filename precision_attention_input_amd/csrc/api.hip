@@ -435,8 +435,8 @@ int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B
     ulp::KStatsLaunch ka{};
     ka.k = static_cast<const uint16_t*>(k);
     char* ws = static_cast<char*>(workspace);
-    ka.mm = reinterpret_cast<float*>(ws);
-    ka.sum = reinterpret_cast<double*>(ws + world_size * B * H * ulp::slots_of(L) * D * 8);
+    ka.sum = reinterpret_cast<double*>(ws);
+    ka.mm = reinterpret_cast<uint16_t*>(ws + world_size * B * H * ulp::slots_of(L) * D * 8);
     ka.minmax = k_minmax;
     ka.amax = k_amax;
     ka.mean_f32 = k_mean_f32;

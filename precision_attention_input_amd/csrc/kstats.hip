@@ -6,14 +6,15 @@
 // raw minimum and maximum: RN is monotone and RN(-x) = -RN(x), so over the rows of a group,
 //   max_rows |RN(k - m)| = max(RN(max_rows k - m), RN(m - min_rows k))      (per channel)
 // which is the same identity derive_k_boundary_amax (description) rests on.  The pass records
-// per (rank, b, head, slot, channel) the raw min / max over the rows the amax runs on and the
-// binary64 sum over the live rows; then
+// per (rank, b, head, slot, channel) the raw min / max over the rows the amax runs on (as
+// the 16-bit inputs themselves) and the binary64 sum over the live rows; then
 //   * kmean_from_sums adds the sums in (rank, slot) order (four contiguous quarters, then the
 //     quarters in order), divides by used in binary64 and rounds to binary32 and to the
 //     dtype (the same definition as ulp_k_mean);
 //   * kamax_from_minmax forms every slot's amax from the min / max and the dtype-rounded
 //     mean, bit-identical to the direct pass;
 // and the boundary min / max of every rank are written by the pass itself.
+#include "order16.h"
 #include "ulp_device.h"
 #include "ulp_kernels.h"
 
@@ -22,7 +23,7 @@ namespace {
 
 struct KStatsParams {
     const uint16_t* k;       // stacked [P, B, L, H, D]
-    float* mm;               // [P, B, H, slots, 2, D] raw min (0) / max (1) over amax rows
+    uint16_t* mm;            // [P, B, H, slots, 2, D] raw min (0) / max (1) over amax rows
     double* sum;             // [P, B, H, slots, D] binary64 sums over live rows
     float* minmax;           // [P, B, H, 2, 2, D] boundary min / max (live rows)
     float* amax;             // [P, B, H, slots]
@@ -32,6 +33,11 @@ struct KStatsParams {
     int P, nhb;
 };
 
+// One 256-thread workgroup per (rank, b, slot, head block), as the statistics kernel: 64
+// rows x 32 sixteen-byte vectors, thread (row lane rl, vector c) reading rows rl + 8i.
+// The raw extremes are kept as Order16 (packed integer operations, no conversion); the
+// sums take the binary64 value of every live element.  The eight row lanes are combined
+// through LDS and the results written by all 256 threads, one (vector, channel) each.
 template <int DT, int D, bool NT>
 __global__ __launch_bounds__(kThreads) void kstats_kernel(KStatsParams p) {
     constexpr int VPH = D / 8;       // 16-byte vectors per head row
@@ -55,95 +61,118 @@ __global__ __launch_bounds__(kThreads) void kstats_kernel(KStatsParams p) {
     const int64_t g = g0 + j;
     const int64_t lo = max((int64_t)kGroup * g, rank * L);
     const int64_t hi = min((int64_t)kGroup * g + kGroup, rank * L + L);
-    // the amax runs over every row of the group except past `used` in the one partial live
-    // group (k_grouped_amax, used_sequence); the sums over live rows
+    // The amax runs over every row of the group except past `used` in the one partial live
+    // group (k_grouped_amax, used_sequence); the sums and the boundary min/max over the live
+    // rows, which are the same rows or none (a group wholly in the zero tail).
     const int64_t amax_hi =
         (p.used < p.S && g == (p.used - 1) / kGroup) ? min(hi, p.used) : hi;
-    const int64_t live_hi = min(hi, p.used);
+    const int nrow = (int)(amax_hi - lo);            // may be <= 0
+    const bool live = min(hi, p.used) > lo;
 
-    const uint16_t* xb = p.k + ((rank * p.B + b) * L * H + head) * D + dv * 8;
-    float mn[8], mx[8];
+    const uint16_t* xr = p.k + (((rank * p.B + b) * L + lo - rank * L) * H + head) * D + dv * 8;
+    Order16 ord[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) ord[w].reset();
+    // Sums start at -0, the identity of IEEE addition (x + -0 = x for every x, +0 included),
+    // so the first addend costs nothing; the mean's sum over slots starts at +0.
     double sm[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        mn[e] = __builtin_inff();
-        mx[e] = -__builtin_inff();
-        sm[e] = 0.0;
-    }
-    uint4 v[8];
+    for (int e = 0; e < 8; ++e) sm[e] = -0.0;
+    if (valid && rl < nrow) {
+        // rows past the range repeat its last row: harmless for the extremes, masked out
+        // of the sums
+        uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t s = lo + rl + 8 * i;
-        v[i] = (valid && s < hi) ? load16<NT>(xb + (s - rank * L) * H * D) : make_uint4(0, 0, 0, 0);
-    }
+        for (int i = 0; i < 8; ++i)
+            v[i] = load16<NT>(xr + (int64_t)min(rl + 8 * i, nrow - 1) * H * D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t s = lo + rl + 8 * i;
-        if (!(valid && s < amax_hi)) continue;
-        float f[8];
-        decode8<DT>(v[i], f);
+        for (int i = 0; i < 8; ++i) {
+            ord[0].add(v[i].x);
+            ord[1].add(v[i].y);
+            ord[2].add(v[i].z);
+            ord[3].add(v[i].w);
+        }
+        if (nrow == kGroup) {                        // a whole live group: no masking
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float cv = f[e] + 0.0f;   // -0 -> +0, every other value unchanged
-            mn[e] = fminf(mn[e], cv);
-            mx[e] = fmaxf(mx[e], cv);
-            if (s < live_hi) sm[e] += (double)f[e];
+            for (int i = 0; i < 8; ++i) {
+                float f[8];
+                decode8<DT>(v[i], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm[e] += (double)f[e];
+            }
+        } else if (live) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float f[8];
+                decode8<DT>(v[i], f);
+                const bool in = rl + 8 * i < nrow;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sm[e] += (double)(in ? f[e] : -0.0f);
+            }
         }
     }
 
-    // Reduce over the 8 row lanes: bit 5 of the lane inside a wave, then the 4 waves in
-    // order through LDS.
-    __shared__ float red_mn[4][32][8];
-    __shared__ float red_mx[4][32][8];
+    // Row lanes: bit 5 of the lane inside a wave (v_permlane32_swap hands each lane the
+    // value of its partner 32 lanes away; merging and adding are symmetric, so both halves
+    // end with the same bits), then the four waves through LDS.
+    __shared__ Order16 red_ord[4][32][4];
     __shared__ double red_sm[4][32][8];
     const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const auto s0 = __builtin_amdgcn_permlane32_swap(ord[w].smax, ord[w].smax, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(ord[w].umin, ord[w].umin, false, false);
+        const auto s2 = __builtin_amdgcn_permlane32_swap(ord[w].umax, ord[w].umax, false, false);
+        ord[w] = merge(Order16{s0[0], s1[0], s2[0]}, Order16{s0[1], s1[1], s2[1]});
+    }
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-        mn[e] = wave_min_xor<32>(mn[e]);
-        mx[e] = wave_max_xor<32>(mx[e]);
-        const double other = __shfl_xor(sm[e], 32, 64);
-        sm[e] = lane < 32 ? sm[e] + other : other + sm[e];
+        const uint64_t u = __builtin_bit_cast(uint64_t, sm[e]);
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32),
+                                                         false, false);
+        sm[e] = __builtin_bit_cast(double, (uint64_t)lo[0] | ((uint64_t)hi[0] << 32)) +
+                __builtin_bit_cast(double, (uint64_t)lo[1] | ((uint64_t)hi[1] << 32));
     }
     if (lane < 32) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            red_mn[wave][c][e] = mn[e];
-            red_mx[wave][c][e] = mx[e];
-            red_sm[wave][c][e] = sm[e];
-        }
+        for (int w = 0; w < 4; ++w) red_ord[wave][c][w] = ord[w];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red_sm[wave][c][e] = sm[e];
     }
     __syncthreads();
-    if (tid >= 32 || !valid) return;
-    float rmn[8], rmx[8];
-    double rsm[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        rmn[e] = fminf(fminf(red_mn[0][c][e], red_mn[1][c][e]),
-                       fminf(red_mn[2][c][e], red_mn[3][c][e]));
-        rmx[e] = fmaxf(fmaxf(red_mx[0][c][e], red_mx[1][c][e]),
-                       fmaxf(red_mx[2][c][e], red_mx[3][c][e]));
-        rsm[e] = ((red_sm[0][c][e] + red_sm[1][c][e]) + red_sm[2][c][e]) + red_sm[3][c][e];
-    }
-    const int64_t rbh = (rank * p.B + b) * H + head;
-    float* o = p.mm + ((rbh * p.slots + j) * 2) * D + dv * 8;
-    double* os = p.sum + (rbh * p.slots + j) * D + dv * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        o[e] = rmn[e];
-        o[D + e] = rmx[e];
-        os[e] = rsm[e];
-    }
-    // Boundary min / max over live rows: the same values, except that a fully padded group
-    // has no live row.
-    const bool empty = lo >= p.used;
-    for (int e2 = 0; e2 < 2; ++e2) {
-        if ((e2 == 0 && j != 0) || (e2 == 1 && j != n - 1)) continue;
-        float* ob = p.minmax + (rbh * 2 + e2) * 2 * D + dv * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            ob[e] = empty ? __builtin_inff() : rmn[e];
-            ob[D + e] = empty ? -__builtin_inff() : rmx[e];
-        }
+
+    // Thread (vector c2, channel pair or channel e2): the four waves in order.
+    const int c2 = tid >> 3, e2 = tid & 7;
+    const int hib2 = c2 / VPH, dv2 = c2 % VPH;
+    const int64_t head2 = (int64_t)hb * HB + hib2;
+    if (head2 >= H) return;
+    const int64_t rbh = (rank * p.B + b) * H + head2;
+    const double s4 =
+        ((red_sm[0][c2][e2] + red_sm[1][c2][e2]) + red_sm[2][c2][e2]) + red_sm[3][c2][e2];
+    p.sum[(rbh * p.slots + j) * D + dv2 * 8 + e2] = s4;
+    if (e2 >= 4) return;
+    const int w2 = e2;                              // channels 2 w2, 2 w2 + 1 of vector c2
+    const Order16 o4 = merge(merge(red_ord[0][c2][w2], red_ord[1][c2][w2]),
+                             merge(red_ord[2][c2][w2], red_ord[3][c2][w2]));
+    const uint32_t mnb = o4.min_bits(), mxb = o4.max_bits();
+    uint16_t* o = p.mm + ((rbh * p.slots + j) * 2) * D + dv2 * 8 + 2 * w2;
+    *reinterpret_cast<uint32_t*>(o) = mnb;
+    *reinterpret_cast<uint32_t*>(o + D) = mxb;
+    // Boundary min / max over live rows, zeros as +0; a group with no live row gives
+    // (+inf, -inf).
+    if (j != 0 && j != n - 1) return;
+    float mn0, mn1, mx0, mx1;
+    decode2<DT>(mnb, mn0, mn1);
+    decode2<DT>(mxb, mx0, mx1);
+    const float inf = __builtin_inff();
+    for (int eb = 0; eb < 2; ++eb) {
+        if ((eb == 0 && j != 0) || (eb == 1 && j != n - 1)) continue;
+        float* ob = p.minmax + (rbh * 2 + eb) * 2 * D + dv2 * 8 + 2 * w2;
+        *reinterpret_cast<float2*>(ob) =
+            live ? make_float2(mn0 + 0.0f, mn1 + 0.0f) : make_float2(inf, inf);
+        *reinterpret_cast<float2*>(ob + D) =
+            live ? make_float2(mx0 + 0.0f, mx1 + 0.0f) : make_float2(-inf, -inf);
     }
 }
 
@@ -223,12 +252,12 @@ __global__ __launch_bounds__(kThreads) void kamax_from_minmax_kernel(KStatsParam
     const int64_t n = last_group(r, p.L) - first_group(r, p.L) + 1;
     float a = -__builtin_inff();
     if (j < n) {
-        const float* o = p.mm + (rbh * p.slots + j) * 2 * D;
+        const uint16_t* o = p.mm + (rbh * p.slots + j) * 2 * D;
         const uint16_t* mp = p.mean_dt + bh * D;
 #pragma unroll
         for (int d = lane; d < D; d += 64) {
             const float m = decode1<DT>(mp[d]);
-            a = fmaxf(a, fmaxf(o[D + d] - m, m - o[d]));
+            a = fmaxf(a, fmaxf(decode1<DT>(o[D + d]) - m, m - decode1<DT>(o[d])));
         }
     }
     a = wave_max_xor<63>(a);

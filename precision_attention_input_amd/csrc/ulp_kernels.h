@@ -63,7 +63,7 @@ struct KMeanLaunch {
 // K statistics and the K mean from one read of the stacked K shards.
 struct KStatsLaunch {
     const uint16_t* k;        // [P, B, L, H, D]
-    float* mm;                // workspace [P, B, H, slots, 2, D]
+    uint16_t* mm;             // workspace [P, B, H, slots, 2, D] raw 16-bit min / max
     double* sum;              // workspace [P, B, H, slots, D]
     float* minmax;            // [P, B, H, 2, 2, D]
     float* amax;              // [P, B, H, slots]
@@ -104,10 +104,10 @@ inline int64_t chunk_section(int64_t B, int64_t L, int64_t h, int64_t D) {
 inline int64_t chunk_scale_section(int64_t B, int64_t L, int64_t h) {
     return align256(4 * B * h * slots_of(L));
 }
-// workspace of the one-read K statistics: raw min / max (fp32) and sums (fp64) per
+// workspace of the one-read K statistics: sums (fp64), then the raw 16-bit min / max, per
 // (rank, b, head, slot, channel)
 inline int64_t kstats_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D, int64_t P) {
-    return P * B * H * slots_of(L) * D * (2 * 4 + 8);
+    return P * B * H * slots_of(L) * D * (8 + 2 * 2);
 }
 inline int64_t chunk_bytes_of(int64_t B, int64_t L, int64_t h, int64_t D) {
     return 3 * chunk_section(B, L, h, D) + 2 * chunk_scale_section(B, L, h);

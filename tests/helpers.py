@@ -55,3 +55,40 @@ def check_amax_against_definition(amax_per_rank, def_amax, w: W.Workload):
         for g in range(g0, g1 + 1):
             if g < def_amax.shape[-1]:
                 assert torch.equal(a[:, :, g - g0], def_amax[:, :, g]), (r, g)
+
+
+def sign_pattern_columns(S, H, D, used, dtype, seed):
+    """[1, S, H, D] values whose channels (per head) cycle through the sign and zero
+    patterns that order statistics on raw 16-bit patterns must get right; rows >= used
+    are +0 (the zero tail)."""
+    g = torch.Generator().manual_seed(seed)
+    fi = torch.finfo(dtype)
+    x = torch.empty(S, H, D, dtype=torch.float64)
+    rows = torch.arange(S, dtype=torch.float64)[:, None]
+    mag = 1.0 + torch.rand(S, H, dtype=torch.float64, generator=g)
+    for c in range(D):
+        kind = c % 10
+        r = mag * (1 + c / D)
+        if kind == 0:
+            col = torch.full((S, H), -0.0, dtype=torch.float64)
+        elif kind == 1:
+            col = torch.where(rows % 2 == 0, -0.0, 0.0).expand(S, H).clone()
+        elif kind == 2:
+            col = -r
+        elif kind == 3:
+            col = r
+        elif kind == 4:
+            col = torch.where(rows % 3 == 0, -0.0, -r)
+        elif kind == 5:
+            col = torch.where(rows % 3 == 0, -0.0, r)
+        elif kind == 6:
+            col = torch.where(rows % 2 == 0, -fi.max, fi.max).expand(S, H).clone()
+        elif kind == 7:
+            col = -fi.smallest_normal * (rows % 7 + 1).expand(S, H) / 8
+        elif kind == 8:
+            col = torch.where(rows % 4 == 0, -0.0, fi.smallest_normal * (rows % 5) / 8).expand(S, H).clone()
+        else:
+            col = torch.randn(S, H, dtype=torch.float64, generator=g)
+        x[:, :, c] = col
+    x[used:] = 0.0
+    return x.to(dtype).unsqueeze(0).contiguous()

@@ -181,7 +181,7 @@ def test_consumer_validation(L):
 
 def test_stats_with_mean_validation(L):
     need = L.ulp_group_stats_with_mean_workspace_bytes(1, 128, 4, 64, 2)
-    assert need == 2 * 1 * 4 * 2 * 64 * 16          # P*B*H*slots*D*(2*4 + 8)
+    assert need == 2 * 1 * 4 * 2 * 64 * 12          # P*B*H*slots*D*(8 + 2*2)
 
     def call(dtype=0, B=1, Lq=128, H=4, D=64, P=2, used=NONE, ws=A, wsb=need, md=A):
         return L.ulp_group_stats_with_mean(A, A, dtype, B, Lq, H, D, P, used, ws, wsb, A, A,

@@ -18,7 +18,7 @@ import precision_attention_input_amd as ulp
 from precision_attention_input_amd import workloads as W
 
 from gpu_helpers import DEV, assert_bits_equal, say
-from helpers import small
+from helpers import sign_pattern_columns, small
 
 pytestmark = pytest.mark.gpu
 
@@ -201,3 +201,17 @@ def test_stats_with_mean_edges(olib, w, used):
     d = W.generate(w)
     _check_with_mean(w, W.stacked_shards(d["K"], w.P).to(DEV),
                      W.stacked_shards(d["Q"], w.P).to(DEV), f"{w.name} used={used}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_stats_with_mean_sign_and_zero_patterns(olib, dtype, D):
+    """Channels of all -0, mixed zeros, one sign, +-max and subnormals (the raw 16-bit
+    ordering of the one-read pass), 65-row shards and a live prefix ending mid-group."""
+    P, L, H, used = 4, 65, 4, 200
+    w = small(P=P, L=L, H=H, D=D, dtype=dtype, used=used)
+    K = sign_pattern_columns(P * L, H, D, used, dtype, 2)
+    Q = sign_pattern_columns(P * L, H, D, used, dtype, 1)
+    _check_with_mean(w, W.stacked_shards(K, P).to(DEV), W.stacked_shards(Q, P).to(DEV),
+                     f"sign patterns {w.name}")
+

@@ -19,7 +19,7 @@ from precision_attention_input_amd import workloads as W
 
 from gpu_helpers import (DEV, assert_bits_equal, compare_all, run_group, run_per_rank, say,
                          sub_heads, to_dev)
-from helpers import small
+from helpers import sign_pattern_columns, small
 
 pytestmark = pytest.mark.gpu
 
@@ -141,43 +141,6 @@ def test_every_input_pattern_through_pack(olib, dtype):
     compare_all(run_group(w, dd), oracle_run(w, d), w, "exhaustive")
 
 
-def _sign_pattern_columns(S, H, D, used, dtype, seed):
-    """[1, S, H, D] values whose channels (per head) cycle through the sign and zero
-    patterns that order statistics on raw 16-bit patterns must get right; rows >= used
-    are +0 (the zero tail)."""
-    g = torch.Generator().manual_seed(seed)
-    fi = torch.finfo(dtype)
-    x = torch.empty(S, H, D, dtype=torch.float64)
-    rows = torch.arange(S, dtype=torch.float64)[:, None]
-    mag = 1.0 + torch.rand(S, H, dtype=torch.float64, generator=g)
-    for c in range(D):
-        kind = c % 10
-        r = mag * (1 + c / D)
-        if kind == 0:
-            col = torch.full((S, H), -0.0, dtype=torch.float64)
-        elif kind == 1:
-            col = torch.where(rows % 2 == 0, -0.0, 0.0).expand(S, H).clone()
-        elif kind == 2:
-            col = -r
-        elif kind == 3:
-            col = r
-        elif kind == 4:
-            col = torch.where(rows % 3 == 0, -0.0, -r)
-        elif kind == 5:
-            col = torch.where(rows % 3 == 0, -0.0, r)
-        elif kind == 6:
-            col = torch.where(rows % 2 == 0, -fi.max, fi.max).expand(S, H).clone()
-        elif kind == 7:
-            col = -fi.smallest_normal * (rows % 7 + 1).expand(S, H) / 8
-        elif kind == 8:
-            col = torch.where(rows % 4 == 0, -0.0, fi.smallest_normal * (rows % 5) / 8).expand(S, H).clone()
-        else:
-            col = torch.randn(S, H, dtype=torch.float64, generator=g)
-        x[:, :, c] = col
-    x[used:] = 0.0
-    return x.to(dtype).unsqueeze(0).contiguous()
-
-
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("D", [64, 128])
 def test_sign_and_zero_patterns_through_statistics(olib, dtype, D):
@@ -189,9 +152,9 @@ def test_sign_and_zero_patterns_through_statistics(olib, dtype, D):
     S = P * L
     w = small(P=P, L=L, H=H, D=D, dtype=dtype, used=used, scale_sequence=used)
     say(f"[sign patterns] {w.name}")
-    d = dict(Q=_sign_pattern_columns(S, H, D, used, dtype, 1),
-             K=_sign_pattern_columns(S, H, D, used, dtype, 2),
-             V=_sign_pattern_columns(S, H, D, used, dtype, 3))
+    d = dict(Q=sign_pattern_columns(S, H, D, used, dtype, 1),
+             K=sign_pattern_columns(S, H, D, used, dtype, 2),
+             V=sign_pattern_columns(S, H, D, used, dtype, 3))
     d["mean"] = W.k_mean_global(d["K"], used, dtype)
     dd = to_dev(d, P)
     ref = oracle_run(w, d)
