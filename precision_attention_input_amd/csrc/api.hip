@@ -414,7 +414,7 @@ int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B
     if (workspace_bytes < need)
         return fail(ULP_EINVAL, "%s: workspace of %lld bytes, %lld needed", fn,
                     (long long)workspace_bytes, (long long)need);
-    if (B * H * D / 64 >= kMaxGrid || (int64_t)world_size * B * H * ulp::slots_of(L) / 4 >= kMaxGrid)
+    if ((B * H * D + 15) / 16 >= kMaxGrid || (int64_t)world_size * B * H * ulp::slots_of(L) / 4 >= kMaxGrid)
         return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
     const int64_t S = world_size * L;
     // Q: grouped amax of raw values and boundary min/max, as ulp_group_stats does

@@ -8,9 +8,9 @@
 // which is the same identity derive_k_boundary_amax (description) rests on.  The pass records
 // per (rank, b, head, slot, channel) the raw min / max over the rows the amax runs on (as
 // the 16-bit inputs themselves) and the binary64 sum over the live rows; then
-//   * kmean_from_sums adds the sums in (rank, slot) order (four contiguous quarters, then the
-//     quarters in order), divides by used in binary64 and rounds to binary32 and to the
-//     dtype (the same definition as ulp_k_mean);
+//   * kmean_from_sums adds the sums in (rank, slot) order (16 contiguous parts, then the
+//     parts in order), divides by used in binary64 and rounds to binary32 and to the dtype
+//     (the same definition as ulp_k_mean);
 //   * kamax_from_minmax forms every slot's amax from the min / max and the dtype-rounded
 //     mean, bit-identical to the direct pass;
 // and the boundary min / max of every rank are written by the pass itself.
@@ -187,21 +187,24 @@ __device__ __forceinline__ uint16_t round_to_dtype(float m) {
 }
 
 // The sums of every rank's touched slots in (rank, slot) order, per (b, head, channel): a
-// workgroup covers 64 consecutive (b, head, channel) values; wave w adds the w-th quarter
-// of the (rank, slot) sequence in order, 8 loads in flight, and the quarters are added in
-// order.
+// workgroup covers 16 consecutive (b, head, channel) values (128-byte loads) and splits the
+// (rank, slot) sequence into 16 contiguous parts, four per wave; each part is added in
+// order with 8 loads in flight, then the parts in order.
+constexpr int kSumParts = 16;
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void kmean_from_sums_kernel(KStatsParams p) {
-    __shared__ double red[3][64];
+    __shared__ double red[kSumParts][16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t i = (int64_t)blockIdx.x * 64 + lane;            // (b, head, d)
+    const int dl = lane & 15, part = wave * 4 + (lane >> 4);
+    const int64_t i = (int64_t)blockIdx.x * 16 + dl;             // (b, head, d)
     const int64_t nv = p.B * p.H * D;
     const int64_t d = i % D, bh = i / D;
     int64_t total = 0;
     for (int r = 0; r < p.P; ++r) total += last_group(r, p.L) - first_group(r, p.L) + 1;
-    const int64_t q0 = total * wave / 4, q1 = total * (wave + 1) / 4;
+    const int64_t q0 = total * part / kSumParts, q1 = total * (part + 1) / kSumParts;
     double sum = 0.0;
-    if (i < nv) {
+    if (i < nv && q0 < q1) {
         // walk (rank, slot) pairs from flat index q0
         int r = 0;
         int64_t base = 0, n = last_group(0, p.L) - first_group(0, p.L) + 1;
@@ -230,10 +233,12 @@ __global__ __launch_bounds__(kThreads) void kmean_from_sums_kernel(KStatsParams 
             if (r < p.P) n = last_group(r, p.L) - first_group(r, p.L) + 1;
         }
     }
-    if (wave > 0) red[wave - 1][lane] = sum;
+    red[part][dl] = sum;
     __syncthreads();
-    if (wave != 0 || i >= nv) return;
-    sum = ((sum + red[0][lane]) + red[1][lane]) + red[2][lane];
+    if (threadIdx.x >= 16 || i >= nv) return;
+    sum = red[0][dl];
+#pragma unroll
+    for (int k = 1; k < kSumParts; ++k) sum += red[k][dl];
     const float mf = (float)(sum / (double)p.used);
     p.mean_f32[i] = mf;
     p.mean_dt[i] = round_to_dtype<DT>(mf);
@@ -291,7 +296,7 @@ hipError_t launch_t(const KStatsLaunch& a, hipStream_t stream) {
         hipLaunchKernelGGL((kstats_kernel<DT, D, false>), g1, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2((unsigned)((a.B * a.H * D + 63) / 64));
+    const dim3 g2((unsigned)((a.B * a.H * D + 15) / 16));
     hipLaunchKernelGGL((kmean_from_sums_kernel<DT, D>), g2, dim3(kThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
