@@ -61,7 +61,8 @@ int check_shape(const char* fn, int dtype, int64_t B, int64_t L, int64_t H, int6
     if (B > lim / L || B * L > lim / H || B * L * H > lim / (D * P))
         return fail(ULP_EINVAL, "%s: problem too large", fn);
     const int64_t slots = ulp::slots_of(L);
-    if (B * slots * ((H + 1) / 2) >= kMaxGrid || B * ((L + 7) / 8) >= kMaxGrid)
+    if (B * slots * ((H + 1) / 2) >= kMaxGrid ||
+        B * ((L + 7) / 8) * ((H * D + 511) / 512) >= kMaxGrid)
         return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
     return ULP_OK;
 }

@@ -36,7 +36,7 @@ struct PackParams {
     int64_t dest_stride, x_rank_stride, amax_rank_stride, send_rank_stride;
     int64_t B, L, H, h, P, slots, sec, ssec;
     uint32_t h_magic;        // floor(x / h) = umulhi(x, h_magic) for x, h < 2^16, h > 1
-    int rank0, nranks, row_blocks;   // row_blocks: per batch entry
+    int rank0, nranks, row_blocks, col_blocks;   // row_blocks: per batch entry
 };
 
 template <int DT>
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     uint8_t* send = p.send + rz * p.send_rank_stride;
     const int tid = threadIdx.x;
 
-    if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (blockIdx.x == 0) {
         // Zero the padding bytes after each section of every destination chunk.
         const int64_t data = p.B * L * h * D;         // bytes of each code section
         const int64_t sdata = 4 * p.B * h * p.slots;  // bytes of each scale section
@@ -134,9 +134,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackParams p) {
     }
 
     // Row (b, l) and 16-element column of this thread; rows < 2^31 and columns < 2^20.
-    const uint32_t b = blockIdx.x / (uint32_t)p.row_blocks;
-    const uint32_t l = (blockIdx.x % (uint32_t)p.row_blocks) * kRows + tid / kCols;
-    const uint32_t col = blockIdx.y * kCols + tid % kCols;
+    // Consecutive workgroups take the column blocks of the same rows, so the workgroups in
+    // flight read whole rows (contiguous memory) rather than one slice of many rows.
+    const uint32_t cblk = blockIdx.x % (uint32_t)p.col_blocks;
+    const uint32_t rblk = blockIdx.x / (uint32_t)p.col_blocks;
+    const uint32_t b = rblk / (uint32_t)p.row_blocks;
+    const uint32_t l = (rblk % (uint32_t)p.row_blocks) * kRows + tid / kCols;
+    const uint32_t col = cblk * kCols + tid % kCols;
     if (l >= (uint32_t)L || col >= (uint32_t)(H * VPH)) return;
     const uint32_t head = col / VPH, dv = col % VPH;
     const uint32_t dst = h == 1 ? head : __umulhi(head, p.h_magic);
@@ -233,8 +237,8 @@ hipError_t launch_t(const PackLaunch& a, hipStream_t stream) {
     p.rank0 = a.rank0;
     p.nranks = a.nranks;
     p.row_blocks = (int)((a.L + kRows - 1) / kRows);
-    const int64_t col_blocks = (a.H * (a.D / 16) + kCols - 1) / kCols;
-    dim3 grid((unsigned)(a.B * p.row_blocks), (unsigned)col_blocks, (unsigned)a.nranks);
+    p.col_blocks = (int)((a.H * (a.D / 16) + kCols - 1) / kCols);
+    dim3 grid((unsigned)(a.B * p.row_blocks * p.col_blocks), 1, (unsigned)a.nranks);
     const int64_t written = a.nranks * 3 * a.B * a.L * a.H * a.D;   // code bytes of this launch
     const bool nt = written > kResidentBytes;
     const dim3 block(kThreads);
