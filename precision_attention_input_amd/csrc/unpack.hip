@@ -89,10 +89,24 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         constexpr int T = 128;                 // time steps per wave tile
         const int wave = tid >> 6, lane = tid & 63;
         const int64_t hw = (h + HPW - 1) / HPW;
-        const int64_t item = bid * 4 + wave;   // (b, head group, tile)
+        const int64_t item = bid * 4 + wave;
         if (item >= p.B * hw * p.v_tiles) return;
-        const int64_t tile = item % p.v_tiles, bj = item / p.v_tiles;
-        const int64_t jw = bj % hw, b = bj / hw;
+        // Wave order: (b, tile, head group) when the received chunks sit in the cache (the
+        // four waves of a workgroup then read whole received rows); (b, head group, tile)
+        // when they stream from HBM (the waves then write consecutive pieces of the same
+        // output rows).
+        int64_t tile, jw, b;
+        if (NTL) {
+            tile = item % p.v_tiles;
+            const int64_t bj = item / p.v_tiles;
+            jw = bj % hw;
+            b = bj / hw;
+        } else {
+            jw = item % hw;
+            const int64_t bt = item / hw;
+            tile = bt % p.v_tiles;
+            b = bt / p.v_tiles;
+        }
         const int db = lane & 7, tb = lane >> 3;
         const int64_t j = jw * HPW + db / (D / 16);
         const int64_t t0 = tile * T + tb * 16;
