@@ -15,11 +15,11 @@
 // tensors, the K mean, 2 x 16 bytes of each of Q, K, V), then quantizes: centered K and bf16
 // Q by the division-free exact decision (quantize_exact in ulp_device.h), fp16 Q by the
 // reciprocal fast path with the exact decision as a per-wave fallback when a quotient lies
-// near a half-integer; V by the E4M3 conversion.  The kernel is VALU-bound on bf16 data, so
-// the per-thread overhead is kept small: 32-bit column arithmetic, one IEEE division and one
-// v_rcp_f32 per tensor.  A 256-thread workgroup covers kRows rows x kCols vectors, so every
-// wave reads and writes whole 1 KB row segments; the grid is (B x row blocks, column
-// blocks, ranks).
+// near a half-integer; V by the E4M3 conversion.  The arithmetic is kept small enough that
+// the kernel is bound by memory alone (32-bit column arithmetic, one IEEE division and one
+// v_rcp_f32 per tensor).  A 256-thread workgroup covers kRows rows x kCols vectors, so every
+// wave reads and writes whole 1 KB row segments; the grid is (B x row blocks x column
+// blocks, ranks), column blocks fastest, so the workgroups in flight cover whole rows.
 #include "ulp_device.h"
 #include "ulp_kernels.h"
 
