@@ -7,25 +7,27 @@
 // that way over the live rows t < used:
 //   score(i, t) = (q8[i] . k8[t]) * q_scale[i / 64] * k_scale[t / 64] / sqrt(D)
 //   out[i, d]   = sum_t softmax_t(score(i, .)) * e4m3(v8[d, t]) * v_scale[d]
-// with the INT8 dot products on v_mfma_i32_16x16x32_i8 (exact int32) and the P.V product on
-// v_mfma_f32_16x16x32_fp8_fp8, P quantized to E4M3 after scaling by 448 (the largest E4M3
-// value), as an FP8 consumer does.  Smooth K needs no correction: removing a per-channel
+// with the INT8 dot products on gfx950's v_mfma_i32_16x16x64_i8 (exact int32) and the P.V
+// product on v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit block scales), P
+// quantized to E4M3 after scaling by 448 (the largest E4M3 value), as an FP8 consumer does.  Smooth K needs no correction: removing a per-channel
 // mean from every key shifts all scores of a query by the same amount.
 //
 // Work decomposition: a 256-thread workgroup owns 64 query rows of one (b, head) -- one Q
-// scale group -- and each wave 16 of them.  Key tiles of 64 rows (one K scale group) and the
-// matching 64 columns of v8 are copied with coalesced 16-byte loads into double-buffered LDS
-// tiles shared by the four waves; the next tile's loads are in flight while the current one
-// is computed.  Both products are computed transposed, so that
-// every per-query quantity lives in the lanes of that query's column:
-//   S^T[key, q] = K . Q^T   (A = 16 keys x 32 channels of k8, B = 32 channels x 16 queries)
-//   O^T[d, q]  += V^T . P^T (A = 16 channels x 32 keys of v8, B = 32 keys x 16 queries)
-// Lane l of an MFMA operand holds row / column l % 16 and k-slice 8 * (l / 16) + [0, 8); the
-// accumulator lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16.  The keys of the P.V
-// product are taken in the order the S^T accumulators hold them (a permutation of the 32
-// keys applied identically to the V^T rows), so no data moves between lanes except the
-// max / sum reductions over the four lanes of a query.  Keys are processed 64 at a time
-// (one K scale group) with the running-max softmax.
+// scale group -- and each wave 16 of them.  Key tiles of 128 rows (two K scale groups) and
+// the matching 128 columns of v8 are copied with coalesced 16-byte loads into
+// double-buffered LDS tiles shared by the four waves; the next tile's loads are in flight
+// while the current one is computed.  Both products are computed transposed, so that every
+// per-query quantity lives in the lanes of that query's column:
+//   S^T[key, q] = K . Q^T   (A = 16 keys x 64 channels of k8, B = 64 channels x 16 queries)
+//   O^T[d, q]  += V^T . P^T (A = 16 channels x 128 keys of v8, B = 128 keys x 16 queries)
+// Lane l of an MFMA operand holds row / column l % 16 and the bytes of lane group l / 16;
+// both instructions pair byte i of lane group g of A with byte i of lane group g of B
+// (checked on gfx950 with an in-bounds one-hot probe), so any assignment of the reduced
+// index to (lane group, byte), the same for both operands, gives the full sum.  The
+// accumulator lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16.  The keys of the
+// P.V product are assigned in the order the S^T accumulators hold them -- byte 4 kb + r of
+// lane group g is key 16 kb + 4 g + r -- and the V^T rows are read in the same order, so no
+// data moves between lanes except the max / sum reductions over the four lanes of a query.
 #include <cmath>
 
 #include "ulp_device.h"
@@ -35,12 +37,11 @@ namespace ulp {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-#ifndef ULP_CONSUMER_KEYS
-#define ULP_CONSUMER_KEYS 128
-#endif
-constexpr int kConsumerKeys = ULP_CONSUMER_KEYS;   // keys per LDS tile: 64 or 128
+constexpr int kConsumerKeys = 128;   // keys per LDS tile: one P.V MFMA per channel block
+constexpr int kUnitScale = 127;      // E8M0 block scale 2^0
 
 struct ConsumerParams {
     const int8_t *q8, *k8;
@@ -51,9 +52,6 @@ struct ConsumerParams {
     float score_scale;   // log2(e) / sqrt(D)
 };
 
-__device__ __forceinline__ int64_t load8(const int8_t* p) {
-    return *reinterpret_cast<const int64_t*>(p);
-}
 
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's lanes), left in all
 // four, with gfx950's lane-swap instructions: v_permlane16_swap exchanges rows 1 and 3 of one
@@ -91,7 +89,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
     constexpr int KT = kConsumerKeys;          // keys per tile
     constexpr int KB = KT / 16;                // 16-key blocks of S^T per tile
-    constexpr int KC = D / 32;                 // 32-channel slices of a Q / K row
+    constexpr int KC = D / 64;                 // 64-channel slices of a Q / K row
     constexpr int CB = D / 16;                 // 16-channel blocks of the output
     using T = ConsumerTiles<D, KT>;
     // global -> LDS copy of one tile: 16 bytes per thread per step
@@ -109,11 +107,12 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
     const int64_t hD = p.h * D;
     const int64_t qi = tile * 64 + wave * 16 + col;   // this lane's query
 
-    // Q^T fragments (B operand): channels 32c + 8 grp + [0, 8) of query qi.
-    int64_t qf[KC];
-    const int8_t* qrow = p.q8 + (b * p.S + qi) * hD + j * D + 8 * grp;
+    // Q^T fragments (B operand): channels 64c + 16 grp + [0, 16) of query qi.
+    v4i qf[KC];
+    const int8_t* qrow = p.q8 + (b * p.S + qi) * hD + j * D + 16 * grp;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) qf[c] = qi < p.S ? load8(qrow + 32 * c) : 0;
+    for (int c = 0; c < KC; ++c)
+        qf[c] = qi < p.S ? *reinterpret_cast<const v4i*>(qrow + 64 * c) : v4i{0, 0, 0, 0};
     const float qs = p.q_scale[(b * p.h + j) * p.W + tile] * p.score_scale;
     const float* ksc = p.k_scale + (b * p.h + j) * p.W;
 
@@ -174,11 +173,11 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = v4i{0, 0, 0, 0};
-            const uint8_t* krow = kl + (16 * kb + col) * T::KROW + 8 * grp;
+            const uint8_t* krow = kl + (16 * kb + col) * T::KROW + 16 * grp;
 #pragma unroll
             for (int c = 0; c < KC; ++c)
-                s[kb] = __builtin_amdgcn_mfma_i32_16x16x32_i8(
-                    *reinterpret_cast<const int64_t*>(krow + 32 * c), qf[c], s[kb], 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                    *reinterpret_cast<const v4i*>(krow + 64 * c), qf[c], s[kb], 0, 0, 0);
         }
         // one K scale per 64 keys; a group past the scale width holds no live key
         float sc[KT / 64];
@@ -215,23 +214,18 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
         psum = quad_sum(psum);
         lsum = lsum * alpha + psum;
         m = mnew;
-        // P^T fragments, 32 keys each: (16 (2 hf) + 4 grp + [0, 4), 16 (2 hf + 1) + 4 grp +
-        // [0, 4)); the V^T rows (channels) are read in the same key order.
-        int64_t pf[KB / 2];
-#pragma unroll
-        for (int hf = 0; hf < KB / 2; ++hf)
-            pf[hf] = (int64_t)pw[2 * hf] | ((int64_t)pw[2 * hf + 1] << 32);
+        // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 16 kb + 4 grp + r; the V^T
+        // rows (channels) are read in the same key order.
+        const v8i pf = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
+                        (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const uint32_t* v32 =
                 reinterpret_cast<const uint32_t*>(vl + (16 * cb + col) * T::VROW + 4 * grp);
-            v4f acc = o[cb] * alpha;
-#pragma unroll
-            for (int hf = 0; hf < KB / 2; ++hf) {
-                const int64_t va = (int64_t)v32[8 * hf] | ((int64_t)v32[8 * hf + 4] << 32);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(va, pf[hf], acc, 0, 0, 0);
-            }
-            o[cb] = acc;
+            const v8i va = {(int)v32[0], (int)v32[4], (int)v32[8], (int)v32[12],
+                            (int)v32[16], (int)v32[20], (int)v32[24], (int)v32[28]};
+            o[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                va, pf, o[cb] * alpha, 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
         if (kt + 1 < ntiles) stash(buf ^ 1);   // the other buffer: nobody reads it now
         __syncthreads();
