@@ -42,6 +42,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kConsumerKeys = 128;   // keys per LDS tile: one P.V MFMA per channel block
 constexpr int kUnitScale = 127;      // E8M0 block scale 2^0
+constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
 
 struct ConsumerParams {
     const int8_t *q8, *k8;
@@ -86,7 +87,8 @@ struct ConsumerTiles {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void consumer_kernel(
+    ConsumerParams p) {
     constexpr int KT = kConsumerKeys;          // keys per tile
     constexpr int KB = KT / 16;                // 16-key blocks of S^T per tile
     constexpr int KC = D / 64;                 // 64-channel slices of a Q / K row
@@ -179,26 +181,45 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
                 s[kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
                     *reinterpret_cast<const v4i*>(krow + 64 * c), qf[c], s[kb], 0, 0, 0);
         }
-        // one K scale per 64 keys; a group past the scale width holds no live key
+        // One K scale per 64 keys, positive (a group past the scale width holds no live key
+        // and takes 1).  The int32 dot products convert exactly; only the last tile can
+        // hold keys past `used`, which become -inf (no maximum, probability exactly 0).
+        // Within a group the largest score is the largest dot product times the scale.
+        const int live = (int)min((int64_t)KT, p.used - t0);   // live keys of this tile
         float sc[KT / 64];
 #pragma unroll
         for (int g = 0; g < KT / 64; ++g) {
             const int64_t gi = t0 / 64 + g;
-            sc[g] = gi < p.W ? qs * ksc[gi] : 0.0f;
+            sc[g] = gi < p.W ? qs * ksc[gi] : 1.0f;
         }
-        float x[KB][4];
-        float tmax = -__builtin_inff();
+        float xf[KB][4];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t t = t0 + 16 * kb + 4 * grp + r;
-                x[kb][r] = t < p.used ? (float)s[kb][r] * sc[kb / 4] : -__builtin_inff();
-                tmax = fmaxf(tmax, x[kb][r]);
-            }
+            for (int r = 0; r < 4; ++r) xf[kb][r] = (float)s[kb][r];
+        if (live < KT) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * kb + 4 * grp + r >= live) xf[kb][r] = -__builtin_inff();
+        }
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int g = 0; g < KT / 64; ++g) {
+            float gmax = -__builtin_inff();
+#pragma unroll
+            for (int kb = 4 * g; kb < 4 * g + 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
+            tmax = fmaxf(tmax, gmax * sc[g]);
+        }
         tmax = quad_max(tmax);
         const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
-        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        // 448 p = exp2(score - mnew + log2(448)), one fma and one exp2 per key; the row sum
+        // is kept in the same 448-scaled units.  The values stay at or below 448 (up to the
+        // exp2 error), so the E4M3 conversion needs no clamp.
+        const float moff = mnew - kLog2_448;
         float psum = 0.0f;
         uint32_t pw[KB];
 #pragma unroll
@@ -206,13 +227,22 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[r] = __builtin_amdgcn_exp2f(x[kb][r] - mnew);
+                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], sc[kb / 4], -moff));
                 psum += pr[r];
             }
-            pw[kb] = e4m3x4(448.0f * pr[0], 448.0f * pr[1], 448.0f * pr[2], 448.0f * pr[3]);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+            pw[kb] = (uint32_t)w;
         }
         psum = quad_sum(psum);
-        lsum = lsum * alpha + psum;
+        // Rescale the running sums only when some query's maximum moved in this wave.
+        if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+            lsum *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+        }
+        lsum += psum;
         m = mnew;
         // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 16 kb + 4 grp + r; the V^T
         // rows (channels) are read in the same key order.
@@ -225,14 +255,14 @@ __global__ __launch_bounds__(kThreads) void consumer_kernel(ConsumerParams p) {
             const v8i va = {(int)v32[0], (int)v32[4], (int)v32[8], (int)v32[12],
                             (int)v32[16], (int)v32[20], (int)v32[24], (int)v32[28]};
             o[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                va, pf, o[cb] * alpha, 0, 0, 0, kUnitScale, 0, kUnitScale);
+                va, pf, o[cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
         if (kt + 1 < ntiles) stash(buf ^ 1);   // the other buffer: nobody reads it now
         __syncthreads();
     }
 
     if (qi >= p.used) return;
-    const float inv = 1.0f / (448.0f * lsum);
+    const float inv = 1.0f / lsum;                 // lsum is in 448-scaled units
     float* orow = p.out + (b * p.used + qi) * hD + j * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
