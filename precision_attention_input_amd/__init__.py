@@ -145,9 +145,11 @@ def unpack_shapes(batch_size, local_sequence, local_heads, head_dim, world_size,
 
 # ------------------------------------------------------------------------- per rank
 
-def k_grouped_amax(k, k_mean_global, *, rank, world_size, used_sequence=None, out=None):
+def k_grouped_amax(k, k_mean_global, *, rank, world_size, used_sequence=None, out=None,
+                   enable_pdl=None):
     """[B, H, slots(L)] fp32 partial amax of |K - k_mean_global| (k_mean_global None: raw
-    values, the Q amax).  flashinfer.comm._ulysses_lowp.k_grouped_amax."""
+    values, the Q amax).  flashinfer.comm._ulysses_lowp.k_grouped_amax.  ``enable_pdl`` is
+    accepted and ignored: launches on one stream run in order on gfx950."""
     _dev(k, k_mean_global, out)
     B, L, H, D = k.shape
     if out is None:
@@ -217,9 +219,10 @@ def _alloc_unpack(device, shapes, lead=()):
 
 
 def unpack_for_sage(recv_u8, *, batch_size, local_sequence, local_heads, head_dim, world_size,
-                    aligned=None, scale_sequence=None, out=None):
+                    aligned=None, scale_sequence=None, out=None, enable_pdl=None):
     """(q8, k8, v8, q_scale, k_scale): INT8 [B,S,h,D] x2, FP8 E4M3 [B,D,h,ceil(S/64)*64],
-    FP32 [B,h,W] x2.  flashinfer.comm._ulysses_lowp.unpack_for_sage."""
+    FP32 [B,h,W] x2.  flashinfer.comm._ulysses_lowp.unpack_for_sage.  ``enable_pdl`` is
+    accepted and ignored: launches on one stream run in order on gfx950."""
     if out is None:
         out = _alloc_unpack(recv_u8.device, unpack_shapes(batch_size, local_sequence,
                                                           local_heads, head_dim, world_size,

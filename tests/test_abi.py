@@ -191,3 +191,29 @@ def test_stats_with_mean_validation(L):
     assert call(D=96) == EUNSUPPORTED
     assert call(used=300) == EINVAL
     assert call(ws=A + 8) == EALIGN
+
+
+def test_page_signatures_are_accepted():
+    """The Python functions take the keyword arguments the three API pages list (plus an
+    optional ``out``), so calls written against the pages run unchanged."""
+    import inspect
+    pages = {
+        "k_grouped_amax": (["k", "k_mean_global"],
+                           ["rank", "world_size", "used_sequence", "enable_pdl"]),
+        "derive_k_boundary_amax": (["grouped_amax", "gathered_minmax", "k_mean_global"],
+                                   ["rank", "local_sequence", "world_size"]),
+        "unpack_for_sage": (["recv_u8"],
+                            ["batch_size", "local_sequence", "local_heads", "head_dim",
+                             "world_size", "aligned", "scale_sequence", "out", "enable_pdl"]),
+    }
+    for name, (positional, keywords) in pages.items():
+        sig = inspect.signature(getattr(ulp, name))
+        params = sig.parameters
+        got_pos = [n for n, p in params.items()
+                   if p.kind == inspect.Parameter.POSITIONAL_OR_KEYWORD]
+        assert got_pos == positional, name
+        for kw in keywords:
+            assert kw in params and params[kw].kind == inspect.Parameter.KEYWORD_ONLY, (name, kw)
+        for n, p in params.items():        # everything beyond the pages is optional
+            if n not in positional and n not in keywords:
+                assert p.default is not inspect.Parameter.empty, (name, n)
