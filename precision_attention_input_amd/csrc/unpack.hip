@@ -113,22 +113,53 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackParams p) {
         if (t0 >= p.spad || j >= h) return;
         const int d0 = (db % (D / 16)) * 16;
 
+        // Rows past the sequence (the zero tail) re-read its last row and are zeroed after
+        // the loads: no load sits in a branch, so all 16 are in flight together.
         uint32_t w[16][4];
-        int64_t s = t0 / L, l = t0 % L;
+        const int64_t hD = h * D;
+        const int64_t tl = min(t0, p.S - 1);
+        const int64_t s0 = tl / L, l0 = tl % L;
         const uint8_t* vsec = recv + 2 * p.sec + ((b * L) * h + j) * D + d0;
+        const uint8_t* rlast = vsec + (p.P - 1) * p.cb + (L - 1) * hD;   // row S - 1
+        if (L >= 16) {
+            // 16 rows cross at most one shard boundary: row i lies in shard s0 while
+            // i < L - l0, else in shard s0 + 1.
+            const uint8_t* rp0 = vsec + s0 * p.cb + l0 * hD;
+            const uint8_t* rp1 = vsec + (s0 + 1) * p.cb + (l0 - L) * hD;
+            const int64_t n0 = L - l0, nrow = p.S - t0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (t0 + i < p.S) x = load16<NTL>(vsec + s * p.cb + l * h * D);
-            w[i][0] = x.x;
-            w[i][1] = x.y;
-            w[i][2] = x.z;
-            w[i][3] = x.w;
-            if (++l == L) {
-                l = 0;
-                ++s;
+            for (int i = 0; i < 16; ++i) {
+                const uint8_t* a = (i < n0 ? rp0 : rp1) + i * hD;
+                const uint4 x = load16<NTL>(i < nrow ? a : rlast);
+                w[i][0] = x.x;
+                w[i][1] = x.y;
+                w[i][2] = x.z;
+                w[i][3] = x.w;
+            }
+        } else {
+            int64_t s = s0, l = l0;
+            const uint8_t* rp = vsec + s * p.cb + l * hD;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint4 x = load16<NTL>(rp);
+                w[i][0] = x.x;
+                w[i][1] = x.y;
+                w[i][2] = x.z;
+                w[i][3] = x.w;
+                if (t0 + i + 1 < p.S) {        // the next row exists: step to it
+                    if (++l == L) {
+                        l = 0;
+                        ++s;
+                        rp = vsec + s * p.cb;
+                    } else {
+                        rp += hD;
+                    }
+                }
             }
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (t0 + i >= p.S) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
         uint32_t o[16][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
