@@ -12,7 +12,9 @@ each timed region (an event recorded between two launches costs about 2 us of GP
 more than 5 % of a small workload's kernel): the K timed steps give ms_per_step; then K
 launches of each kernel alone give its average duration (pack_ms, unpack_ms, stats_ms,
 derive_ms; the roofline figure uses pack_ms), and K back-to-back pack+unpack pairs give
-the reported value: pack+unpack algorithmic bytes / average pair time.  The global K mean
+the reported value: pack+unpack algorithmic bytes / average pair time.  Each of these
+per-kernel loops is preceded by three untimed calls and timed five times; the median loop
+is reported.  The global K mean
 (an input of the step) is timed the same way, as k_mean GB/s.  Prints one JSON line.
 """
 from __future__ import annotations
@@ -21,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+REPS = 5                        # timed loops per kernel figure (the median loop is reported)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["precision_attention_input_amd/csrc/pack.hip",
                   "precision_attention_input_amd/csrc/ulp_device.h"]
@@ -308,18 +312,26 @@ def main():
         pack(s)
         unpack(s)
 
-    def timed(fn, n):
+    def timed(fn, n, reps=1, warm=3):
         """Average ms per call over n back-to-back calls on rotating buffer sets, with HIP
         events (on the current stream, where every launch goes) only at the two ends of the
-        region: an event recorded between two launches costs about 2 us of GPU time."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for i in range(n):
+        region: an event recorded between two launches costs about 2 us of GPU time.  `warm`
+        untimed calls of the same loop come first; with reps > 1 the loop of n calls is
+        timed reps times and the median loop is returned (one late dispatch or clock dip in
+        a loop of small kernels otherwise moves a single loop's average by a percent)."""
+        for i in range(warm):
             fn(sets[i % nsets])
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        loops = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(n):
+                fn(sets[i % nsets])
+            e1.record()
+            torch.cuda.synchronize()
+            loops.append(e0.elapsed_time(e1) / n)
+        return statistics.median(loops)
 
     for i in range(max(args.warmup, nsets)):      # every set gets valid statistics
         step(sets[i % nsets])
@@ -329,16 +341,17 @@ def main():
     K = args.steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ms = timed(step, K)
+    step_ms = timed(step, K, warm=0)           # exactly the K steps (warm-up done above)
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
 
-    # Each kernel on its own, and pack+unpack as a pair, K launches each on the same sets.
-    stats_ms = timed(stats, K)
-    derive_ms = timed(derive, K)
-    pack_ms = timed(pack, K)
-    unpack_ms = timed(unpack, K)
-    pu_ms = timed(pack_unpack, K)
+    # Each kernel on its own, and pack+unpack as a pair: loops of K launches on the same
+    # sets, the median of REPS loops.
+    stats_ms = timed(stats, K, REPS)
+    derive_ms = timed(derive, K, REPS)
+    pack_ms = timed(pack, K, REPS)
+    unpack_ms = timed(unpack, K, REPS)
+    pu_ms = timed(pack_unpack, K, REPS)
 
     # The global K mean, an input of the step (formed once per K tensor), timed on its own.
     ws = torch.empty(int(ulp.lib().ulp_k_mean_workspace_bytes(B, L, H, D, P, ulp._none(w.used))),
