@@ -221,6 +221,10 @@ def main():
                     help="time the MFMA consumer check (INT8 Q.K, FP8 P.V attention over every "
                          "destination's unpacked tensors) instead of the path; prints its own "
                          "JSON line (TFLOP/s against the 5.0 PFLOP/s int8/fp8 dense peak)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture every timed loop into a HIP graph once and time its replays "
+                         "(removes the host's per-launch cost; matters for launch-bound "
+                         "workloads such as the tiny one)")
     ap.add_argument("--v-scale", action="store_true",
                     help="pass a caller-held [B,H,D] V scale to the pack (V divided before "
                          "E4M3); the default converts V unscaled")
@@ -321,16 +325,32 @@ def main():
         a loop of small kernels otherwise moves a single loop's average by a percent)."""
         for i in range(warm):
             fn(sets[i % nsets])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        loops = []
-        for _ in range(reps):
-            torch.cuda.synchronize()
-            e0.record()
+
+        def loop():
             for i in range(n):
                 fn(sets[i % nsets])
+
+        run = loop
+        if args.graph:
+            # the n calls captured once into a HIP graph and replayed: no host launch cost
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                loop()
+            graph.replay()                      # one untimed replay
+            run = graph.replay
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        loops, walls = [], []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            w0 = time.perf_counter()
+            e0.record()
+            run()
             e1.record()
             torch.cuda.synchronize()
+            walls.append((time.perf_counter() - w0) * 1e3 / n)
             loops.append(e0.elapsed_time(e1) / n)
+        timed.wall_ms = statistics.median(walls)
         return statistics.median(loops)
 
     for i in range(max(args.warmup, nsets)):      # every set gets valid statistics
@@ -339,11 +359,8 @@ def main():
 
     # The timed steps: the whole path, K steps.
     K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     step_ms = timed(step, K, warm=0)           # exactly the K steps (warm-up done above)
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / K
+    ms_per_step = timed.wall_ms                # host clock around them, synchronized
 
     # Each kernel on its own, and pack+unpack as a pair: loops of K launches on the same
     # sets, the median of REPS loops.
@@ -417,7 +434,8 @@ def main():
         "config": {"workload": w.name, "B": B, "world_size": P, "local_sequence": L,
                    "heads": H, "head_dim": D, "used_sequence": w.used,
                    "scale_sequence": w.scale_sequence, "aligned": w.aligned,
-                   "v_scale": bool(args.v_scale), "buffer_sets": nsets},
+                   "v_scale": bool(args.v_scale), "buffer_sets": nsets,
+                   "hip_graph": bool(args.graph)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "pack_unpack_bytes": pu_bytes,
         "pack_unpack_ms": round(pu_ms, 5),
