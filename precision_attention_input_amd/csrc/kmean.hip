@@ -53,25 +53,41 @@ __global__ __launch_bounds__(kThreads) void kmean_partial_kernel(KMeanParams p) 
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     if (col < p.HD && t0 < t1) {
         int64_t r = t0 / p.L, l = t0 - r * p.L;   // shard and local row of global row t
+        const uint16_t* kc = p.k + col;
         for (int64_t t = t0; t < t1; t += 8) {
             uint4 v[8];
+            if (l + 8 <= p.L && t + 8 <= t1) {
+                // the whole batch in one shard and in the range (the common case; the
+                // test is the same for every lane): consecutive rows, one stride apart
+                const uint16_t* rp = kc + ((r * p.B + b) * p.L + l) * p.HD;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int64_t ri = r, li = l + i;
-                while (li >= p.L) {        // 8 rows span at most 8 shard boundaries
-                    li -= p.L;
-                    ++ri;
+                for (int i = 0; i < 8; ++i) v[i] = load16<NT>(rp + i * p.HD);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float f[8];
+                    decode8<DT>(v[i], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
                 }
-                v[i] = t + i < t1 ? load16<NT>(p.k + ((ri * p.B + b) * p.L + li) * p.HD + col)
-                                  : make_uint4(0, 0, 0, 0);
-            }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (t + i >= t1) break;
-                float f[8];
-                decode8<DT>(v[i], f);
+                for (int i = 0; i < 8; ++i) {
+                    int64_t ri = r, li = l + i;
+                    while (li >= p.L) {    // 8 rows span at most 8 shard boundaries
+                        li -= p.L;
+                        ++ri;
+                    }
+                    v[i] = t + i < t1 ? load16<NT>(kc + ((ri * p.B + b) * p.L + li) * p.HD)
+                                      : make_uint4(0, 0, 0, 0);
+                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+                for (int i = 0; i < 8; ++i) {
+                    if (t + i >= t1) break;
+                    float f[8];
+                    decode8<DT>(v[i], f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
+                }
             }
             l += 8;
             while (l >= p.L) {
