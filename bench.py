@@ -215,7 +215,9 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="workload name (default: the unaligned padded fp16 workload)")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=20,
+                    help="repetitions of the whole workload through the CPU oracle (about 10 s "
+                         "of single-threaded CPU work on the default workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--consumer", action="store_true",
                     help="time the MFMA consumer check (INT8 Q.K, FP8 P.V attention over every "
