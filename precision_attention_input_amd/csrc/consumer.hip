@@ -41,6 +41,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kConsumerKeys = 128;   // keys per LDS tile: one P.V MFMA per channel block
+// Waves (16 queries each) per workgroup: they share every K / V tile in LDS, so more waves
+// mean fewer tile loads per query; 8 measured best at D = 128, 4 at D = 64.
+template <int D>
+constexpr int consumer_waves() { return D == 128 ? 8 : 4; }
 constexpr int kUnitScale = 127;      // E8M0 block scale 2^0
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
 
@@ -87,7 +91,8 @@ struct ConsumerTiles {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void consumer_kernel(
+__global__ __launch_bounds__(64 * consumer_waves<D>()) __attribute__((amdgpu_waves_per_eu(2)))
+void consumer_kernel(
     ConsumerParams p) {
     constexpr int KT = kConsumerKeys;          // keys per tile
     constexpr int KB = KT / 16;                // 16-key blocks of S^T per tile
@@ -97,9 +102,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // global -> LDS copy of one tile: 16 bytes per thread per step
     constexpr int KV = D / 16;                 // 16-byte pieces of a K row
     constexpr int VV = KT / 16;                // 16-byte pieces of a V row
-    constexpr int KSTEPS = KT * KV / kThreads;
-    constexpr int VSTEPS = D * VV / kThreads;
-    static_assert(KSTEPS * kThreads == KT * KV && VSTEPS * kThreads == D * VV, "tile split");
+    constexpr int NT = 64 * consumer_waves<D>();   // threads per workgroup
+    constexpr int NQ = 16 * consumer_waves<D>();   // queries per workgroup
+    constexpr int KSTEPS = KT * KV / NT;
+    constexpr int VSTEPS = D * VV / NT;
+    static_assert(KSTEPS * NT == KT * KV && VSTEPS * NT == D * VV, "tile split");
     __shared__ __align__(16) T tl;
 
     const int tid = threadIdx.x;
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int col = lane & 15, grp = lane >> 4;
     const int64_t tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int64_t hD = p.h * D;
-    const int64_t qi = tile * 64 + wave * 16 + col;   // this lane's query
+    const int64_t qi = tile * NQ + wave * 16 + col;   // this lane's query
 
     // Q^T fragments (B operand): channels 64c + 16 grp + [0, 16) of query qi.
     v4i qf[KC];
@@ -115,7 +122,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int c = 0; c < KC; ++c)
         qf[c] = qi < p.S ? *reinterpret_cast<const v4i*>(qrow + 64 * c) : v4i{0, 0, 0, 0};
-    const float qs = p.q_scale[(b * p.h + j) * p.W + tile] * p.score_scale;
+    // Q scale group of this wave's queries; a wave wholly past `used` (it still takes part
+    // in the shared tile loads and barriers, its outputs are not stored) reads the last one.
+    const int64_t qg = min((tile * NQ + wave * 16) / 64, p.W - 1);
+    const float qs = p.q_scale[(b * p.h + j) * p.W + qg] * p.score_scale;
     const float* ksc = p.k_scale + (b * p.h + j) * p.W;
 
     v4f o[CB];
@@ -135,14 +145,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto fetch = [&](int64_t t0) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const int e = s * kThreads + tid, row = e / KV, piece = e % KV;
+            const int e = s * NT + tid, row = e / KV, piece = e % KV;
             const int64_t t = t0 + row;
             kr[s] = t < p.used ? *reinterpret_cast<const uint4*>(kg + t * hD + 16 * piece)
                                : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * kThreads + tid, d = e / VV, piece = e % VV;
+            const int e = s * NT + tid, d = e / VV, piece = e % VV;
             const int64_t t = t0 + 16 * piece;
             vr[s] = t < p.spad ? *reinterpret_cast<const uint4*>(vg + d * vrow + t)
                                : make_uint4(0, 0, 0, 0);
@@ -151,12 +161,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     auto stash = [&](int buf) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const int e = s * kThreads + tid, row = e / KV, piece = e % KV;
+            const int e = s * NT + tid, row = e / KV, piece = e % KV;
             *reinterpret_cast<uint4*>(&tl.k[buf][row * T::KROW + 16 * piece]) = kr[s];
         }
 #pragma unroll
         for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * kThreads + tid, d = e / VV, piece = e % VV;
+            const int e = s * NT + tid, d = e / VV, piece = e % VV;
             *reinterpret_cast<uint4*>(&tl.v[buf][d * T::VROW + 16 * piece]) = vr[s];
         }
     };
@@ -297,11 +307,15 @@ hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream) {
     p.W = a.W;
     p.used = a.used;
     p.score_scale = (float)(1.4426950408889634 / std::sqrt((double)a.D));
-    dim3 grid((unsigned)((a.used + 63) / 64), (unsigned)a.h, (unsigned)a.B);
-    if (a.D == 64)
-        hipLaunchKernelGGL((consumer_kernel<64>), grid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((consumer_kernel<128>), grid, dim3(kThreads), 0, stream, p);
+    if (a.D == 64) {
+        constexpr int nq = 16 * consumer_waves<64>();
+        const dim3 grid((unsigned)((a.used + nq - 1) / nq), (unsigned)a.h, (unsigned)a.B);
+        hipLaunchKernelGGL((consumer_kernel<64>), grid, dim3(4 * nq), 0, stream, p);
+    } else {
+        constexpr int nq = 16 * consumer_waves<128>();
+        const dim3 grid((unsigned)((a.used + nq - 1) / nq), (unsigned)a.h, (unsigned)a.B);
+        hipLaunchKernelGGL((consumer_kernel<128>), grid, dim3(4 * nq), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
