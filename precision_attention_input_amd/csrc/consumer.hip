@@ -24,10 +24,15 @@
 // both instructions pair byte i of lane group g of A with byte i of lane group g of B
 // (checked on gfx950 with an in-bounds one-hot probe), so any assignment of the reduced
 // index to (lane group, byte), the same for both operands, gives the full sum.  The
-// accumulator lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16.  The keys of the
-// P.V product are assigned in the order the S^T accumulators hold them -- byte 4 kb + r of
-// lane group g is key 16 kb + 4 g + r -- and the V^T rows are read in the same order, so no
-// data moves between lanes except the max / sum reductions over the four lanes of a query.
+// accumulator lane l holds rows 4 * (l / 16) + [0, 4) of column l % 16.  The rows of the
+// K operand are fed in a permuted order -- row i of 16-key block kb is key
+// 32 (i / 4) + 4 kb + i % 4 -- so the accumulators of lane group g hold the 32 consecutive
+// keys 32 g + [0, 32) (byte 4 kb + r = key 32 g + 4 kb + r): the lane's packed P bytes are
+// then the P.V product's B operand in key order, the V^T fragment is 32 consecutive bytes
+// of a channel row, and each lane's keys share one K scale group.  No data moves between
+// lanes except the max / sum reductions over the four lanes of a query.  The permutation is
+// applied once, when a K row is stored in LDS (slot 16 kb + 4 q + r for key 32 q + 4 kb + r),
+// so every fragment read covers 16 consecutive padded rows.
 #include <cmath>
 
 #include "ulp_device.h"
@@ -162,7 +167,8 @@ void consumer_kernel(
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             const int e = s * NT + tid, row = e / KV, piece = e % KV;
-            *reinterpret_cast<uint4*>(&tl.k[buf][row * T::KROW + 16 * piece]) = kr[s];
+            const int slot = 16 * ((row & 31) >> 2) + 4 * (row >> 5) + (row & 3);
+            *reinterpret_cast<uint4*>(&tl.k[buf][slot * T::KROW + 16 * piece]) = kr[s];
         }
 #pragma unroll
         for (int s = 0; s < VSTEPS; ++s) {
@@ -180,7 +186,11 @@ void consumer_kernel(
         if (kt + 1 < ntiles) fetch(t0 + KT);   // in flight while this tile is computed
         const uint8_t* kl = tl.k[buf];
         const uint8_t* vl = tl.v[buf];
-        // S^T for keys t0 + 16 kb + [0, 16): lane holds keys t0 + 16 kb + 4 grp + r.
+        // S^T, 16 keys per MFMA: row i of block kb is key 32 (i / 4) + 4 kb + i % 4 of the
+        // tile, so the accumulator rows 4 grp + r of every block hold this lane's 32
+        // consecutive keys 32 grp + 4 kb + r.
+        // (The stash stores key row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block
+        // kb reads 16 consecutive slots: no bank conflicts.)
         v4i s[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -191,17 +201,13 @@ void consumer_kernel(
                 s[kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
                     *reinterpret_cast<const v4i*>(krow + 64 * c), qf[c], s[kb], 0, 0, 0);
         }
-        // One K scale per 64 keys, positive (a group past the scale width holds no live key
-        // and takes 1).  The int32 dot products convert exactly; only the last tile can
-        // hold keys past `used`, which become -inf (no maximum, probability exactly 0).
-        // Within a group the largest score is the largest dot product times the scale.
+        // The lane's keys lie in one 64-key K scale group (positive; a group past the scale
+        // width holds no live key and takes 1), so its largest score is its largest dot
+        // product times that scale.  The int32 dot products convert exactly; only the last
+        // tile can hold keys past `used`, which become -inf (no maximum, probability 0).
         const int live = (int)min((int64_t)KT, p.used - t0);   // live keys of this tile
-        float sc[KT / 64];
-#pragma unroll
-        for (int g = 0; g < KT / 64; ++g) {
-            const int64_t gi = t0 / 64 + g;
-            sc[g] = gi < p.W ? qs * ksc[gi] : 1.0f;
-        }
+        const int64_t gi = t0 / 64 + (grp >> 1);
+        const float scl = gi < p.W ? qs * ksc[gi] : 1.0f;
         float xf[KB][4];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -212,18 +218,14 @@ void consumer_kernel(
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (16 * kb + 4 * grp + r >= live) xf[kb][r] = -__builtin_inff();
+                    if (32 * grp + 4 * kb + r >= live) xf[kb][r] = -__builtin_inff();
         }
-        float tmax = -__builtin_inff();
+        float gmax = -__builtin_inff();
 #pragma unroll
-        for (int g = 0; g < KT / 64; ++g) {
-            float gmax = -__builtin_inff();
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int kb = 4 * g; kb < 4 * g + 4; ++kb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
-            tmax = fmaxf(tmax, gmax * sc[g]);
-        }
+            for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
+        float tmax = gmax * scl;
         tmax = quad_max(tmax);
         const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
         // 448 p = exp2(score - mnew + log2(448)), one fma and one exp2 per key; the row sum
@@ -237,7 +239,7 @@ void consumer_kernel(
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], sc[kb / 4], -moff));
+                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], scl, -moff));
                 psum += pr[r];
             }
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
@@ -254,16 +256,17 @@ void consumer_kernel(
         }
         lsum += psum;
         m = mnew;
-        // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 16 kb + 4 grp + r; the V^T
-        // rows (channels) are read in the same key order.
+        // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 32 grp + 4 kb + r, i.e. in
+        // key order; the V^T rows (channels) supply the same 32 consecutive keys.
         const v8i pf = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
                         (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const uint32_t* v32 =
-                reinterpret_cast<const uint32_t*>(vl + (16 * cb + col) * T::VROW + 4 * grp);
-            const v8i va = {(int)v32[0], (int)v32[4], (int)v32[8], (int)v32[12],
-                            (int)v32[16], (int)v32[20], (int)v32[24], (int)v32[28]};
+            const uint4* v16 =
+                reinterpret_cast<const uint4*>(vl + (16 * cb + col) * T::VROW + 32 * grp);
+            const uint4 va0 = v16[0], va1 = v16[1];
+            const v8i va = {(int)va0.x, (int)va0.y, (int)va0.z, (int)va0.w,
+                            (int)va1.x, (int)va1.y, (int)va1.z, (int)va1.w};
             o[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 va, pf, o[cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
