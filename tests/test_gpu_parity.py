@@ -336,7 +336,7 @@ def test_invalid_arguments_launch_nothing(olib):
 
 # ----------------------------------------------------------------- seeded random shapes
 
-def _random_cases(n=24, seed=2024):
+def _random_cases(n=96, seed=2024):
     g = torch.Generator().manual_seed(seed)
     cases = []
     for i in range(n):
