@@ -34,7 +34,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
 REPS = 5                        # timed loops per kernel figure (the median loop is reported)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["precision_attention_input_amd/csrc/pack.hip",
-                  "precision_attention_input_amd/csrc/ulp_device.h"]
+                  "precision_attention_input_amd/csrc/ulp_device.h",
+                  "precision_attention_input_amd/csrc/pack_device.h"]
 
 
 def algorithmic_bytes(w, v_scale: bool = False) -> dict:
@@ -406,6 +407,30 @@ def main():
     sm_sep_ms = timed(stats_mean_separate, K)
     sm_one_ms = timed(stats_mean_one_read, K)
 
+    # The one-read step: statistics and the pack of every slot that derive cannot change
+    # from one read of Q, K and V, then derive, then the pack of the slots that waited for
+    # derive, then the unpack (same outputs as the step above).
+    def stats_pack(s):
+        ulp.group_stats_pack(s["Q"], s["K"], s["V"], s["mean"], world_size=P,
+                             used_sequence=w.used, v_scale=vsc, out=s["stats"],
+                             group=s["group"])
+
+    def pack_deferred(s):
+        ulp.group_pack_deferred(s["Q"], s["K"], s["mean"], s["stats"][0], s["stats"][1],
+                                world_size=P, group=s["group"], used_sequence=w.used)
+
+    def one_read_step(s):
+        stats_pack(s)
+        derive(s)
+        pack_deferred(s)
+        unpack(s)
+
+    for i in range(max(args.warmup, nsets)):
+        one_read_step(sets[i % nsets])
+    or_step_ms = timed(one_read_step, K, REPS)
+    sp_ms = timed(stats_pack, K, REPS)
+    pd_ms = timed(pack_deferred, K, REPS)
+
     pu_bytes = nb["pack"] + nb["unpack"]
     value = pu_bytes / (pu_ms * 1e-3) / 1e9
     pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
@@ -450,6 +475,10 @@ def main():
         "k_mean_gbps": round(nb["k_mean"] / (k_mean_ms * 1e-3) / 1e9, 2),
         "stats_with_mean_ms": {"k_mean_then_stats": round(sm_sep_ms, 5),
                                "one_read_of_k": round(sm_one_ms, 5)},
+        "one_read_step_ms": {"step": round(or_step_ms, 5),
+                             "stats_pack": round(sp_ms, 5),
+                             "pack_deferred": round(pd_ms, 5),
+                             "stats_pack_gbps": round(nb["pack"] / (sp_ms * 1e-3) / 1e9, 2)},
         "step_ms_events": round(step_ms, 5),
         "step_gbps": round((pu_bytes + nb["stats"]) / (step_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),

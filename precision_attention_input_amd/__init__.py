@@ -22,7 +22,8 @@ __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
     "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
-    "group_stats_with_mean", "consumer_attention",
+    "group_stats_with_mean", "consumer_attention", "stats_pack", "pack_deferred",
+    "group_stats_pack", "group_pack_deferred",
     "unpack_shapes",
 ]
 
@@ -74,6 +75,14 @@ def lib():
             "ulp_group_stats_with_mean_workspace_bytes": ([i64, i64, i64, i64, i32], i64),
             "ulp_group_stats_with_mean": ([vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, i64,
                                            vp, vp, vp, vp, vp, vp, vp], i32),
+            "ulp_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i32, i64, vp,
+                                vp, vp, vp, vp, i64, vp], i32),
+            "ulp_pack_deferred": ([vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i32, i64,
+                                   vp, i64, vp], i32),
+            "ulp_group_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i64, vp,
+                                      vp, vp, vp, vp, vp], i32),
+            "ulp_group_pack_deferred": ([vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i64,
+                                         vp, vp], i32),
             "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                         vp, vp], i32),
         }
@@ -298,6 +307,81 @@ def group_unpack(group, *, batch_size, local_sequence, local_heads, head_dim, wo
                                   head_dim, world_size, _none(aligned), _none(scale_sequence),
                                   _p(q8), _p(k8), _p(v8), _p(qs), _p(ks), _stream(group)))
     return tuple(out)
+
+
+# ------------------------------------------------------------------------- one-read step
+
+def _stats_out(lead, B, L, H, D, device):
+    f = dict(dtype=torch.float32, device=device)
+    return (torch.empty(*lead, B, H, slots(L), **f), torch.empty(*lead, B, H, slots(L), **f),
+            torch.empty(*lead, B, H, 2, 2, D, **f), torch.empty(*lead, B, H, 2, 2, D, **f))
+
+
+def stats_pack(q, k, v, k_mean_global, *, rank, world_size, used_sequence=None, v_scale=None,
+               out=None, send=None, dest_stride=None):
+    """One rank's grouped amax (Q raw, K centered), boundary min/max and the pack of every
+    slot that derive cannot change, from one read of q, k, v [B,L,H,D].  Returns
+    ((q_amax, k_amax, q_minmax, k_minmax), send); finish with derive_k_boundary_amax on
+    both amax and pack_deferred."""
+    B, L, H, D = q.shape
+    if out is None:
+        out = _stats_out((), B, L, H, D, q.device)
+    cb = chunk_bytes(B, L, H // world_size, D)
+    if send is None:
+        send = torch.empty(world_size, cb, dtype=torch.uint8, device=q.device)
+        dest_stride = cb
+    _dev(q, k, v, k_mean_global, v_scale, *out)
+    _v_scale(v_scale, B, H, D)
+    qa, ka, qm, km = out
+    _check(lib().ulp_stats_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(v_scale),
+                                B, L, H, D, rank, world_size, _none(used_sequence), _p(qa),
+                                _p(ka), _p(qm), _p(km), _p(send), dest_stride or cb,
+                                _stream(q)))
+    return tuple(out), send
+
+
+def pack_deferred(q, k, k_mean_global, q_amax, k_amax, *, rank, world_size, send,
+                  used_sequence=None, dest_stride=None):
+    """The pack of the slots that waited for derive (q_amax, k_amax after derive)."""
+    _dev(q, k, k_mean_global, q_amax, k_amax)
+    B, L, H, D = q.shape
+    cb = chunk_bytes(B, L, H // world_size, D)
+    _check(lib().ulp_pack_deferred(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
+                                   _p(k_amax), B, L, H, D, rank, world_size,
+                                   _none(used_sequence), _p(send), dest_stride or cb,
+                                   _stream(q)))
+    return send
+
+
+def group_stats_pack(q, k, v, k_mean_global, *, world_size, used_sequence=None, v_scale=None,
+                     out=None, group=None):
+    """stats_pack for every rank of stacked shards [P,B,L,H,D]; returns ((q_amax, k_amax
+    [P,B,H,slots], q_minmax, k_minmax [P,B,H,2,2,D]), group).  Then group_derive and
+    group_pack_deferred."""
+    P, B, L, H, D = q.shape
+    if out is None:
+        out = _stats_out((P,), B, L, H, D, q.device)
+    if group is None:
+        group = group_buffer(B, L, H, D, world_size, q.device)
+    _dev(q, k, v, k_mean_global, v_scale, group, *out)
+    _v_scale(v_scale, B, H, D)
+    qa, ka, qm, km = out
+    _check(lib().ulp_group_stats_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q),
+                                      _p(v_scale), B, L, H, D, world_size,
+                                      _none(used_sequence), _p(qa), _p(ka), _p(qm), _p(km),
+                                      _p(group), _stream(q)))
+    return tuple(out), group
+
+
+def group_pack_deferred(q, k, k_mean_global, q_amax, k_amax, *, world_size, group,
+                        used_sequence=None):
+    """pack_deferred for every rank (after group_derive)."""
+    _dev(q, k, k_mean_global, q_amax, k_amax, group)
+    P, B, L, H, D = q.shape
+    _check(lib().ulp_group_pack_deferred(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
+                                         _p(k_amax), B, L, H, D, world_size,
+                                         _none(used_sequence), _p(group), _stream(q)))
+    return group
 
 
 # ------------------------------------------------------------------------- global K mean

@@ -345,6 +345,105 @@ int ulp_group_pack(const void* q, const void* k, const void* v, const void* k_me
     return launched(ulp::launch_pack(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Shared part of the one-read statistics + pack entry points (phase 0) and of the pack of
+// the slots that wait for derive (phase 1).
+static int stats_pack_common(const char* fn, int phase, const void* q, const void* k,
+                             const void* v, const void* k_mean, int dtype,
+                             const float* v_scale, int64_t B, int64_t L, int64_t H, int64_t D,
+                             int rank, int nranks, int world_size, int64_t used_sequence,
+                             float* q_amax, float* k_amax, float* q_minmax, float* k_minmax,
+                             uint8_t* send, int64_t dest_stride_bytes,
+                             int64_t send_rank_stride, void* stream) {
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, rank, nranks == 1));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    TRY(check_ptr(fn, "q", q));
+    TRY(check_ptr(fn, "k", k));
+    if (phase == 0) TRY(check_ptr(fn, "v", v));
+    TRY(check_ptr(fn, "k_mean", k_mean));
+    TRY(check_ptr(fn, "q_amax", q_amax));
+    TRY(check_ptr(fn, "k_amax", k_amax));
+    if (phase == 0) {
+        TRY(check_ptr(fn, "q_minmax", q_minmax));
+        TRY(check_ptr(fn, "k_minmax", k_minmax));
+        if (v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
+    }
+    TRY(check_ptr(fn, "send", send));
+    const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
+    if (dest_stride_bytes % 256 != 0)
+        return fail(ULP_EALIGN, "%s: dest_stride_bytes %lld is not a multiple of 256", fn,
+                    (long long)dest_stride_bytes);
+    if (dest_stride_bytes < cb)
+        return fail(ULP_EINVAL, "%s: dest_stride_bytes %lld is smaller than the chunk (%lld)",
+                    fn, (long long)dest_stride_bytes, (long long)cb);
+    if (B * ulp::slots_of(L) * (H * D / 128) >= kMaxGrid)
+        return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
+    ulp::StatsPackLaunch a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.v = static_cast<const uint16_t*>(v);
+    a.mean = static_cast<const uint16_t*>(k_mean);
+    a.v_scale = v_scale;
+    a.q_amax = q_amax;
+    a.k_amax = k_amax;
+    a.q_minmax = q_minmax;
+    a.k_minmax = k_minmax;
+    a.send = send;
+    a.dest_stride = dest_stride_bytes;
+    a.x_rank_stride = B * L * H * D;
+    a.amax_rank_stride = B * H * ulp::slots_of(L);
+    a.minmax_rank_stride = B * H * 4 * D;
+    a.send_rank_stride = send_rank_stride;
+    a.B = B; a.L = L; a.H = H; a.D = D; a.P = world_size;
+    a.used = used_or_s(used_sequence, world_size * L);
+    a.rank0 = nranks == 1 ? rank : 0;
+    a.nranks = nranks;
+    a.dtype = dtype;
+    a.phase = phase;
+    return launched(ulp::launch_stats_pack(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int ulp_stats_pack(const void* q, const void* k, const void* v, const void* k_mean, int dtype,
+                   const float* v_scale, int64_t B, int64_t L, int64_t H, int64_t D, int rank,
+                   int world_size, int64_t used_sequence, float* q_amax, float* k_amax,
+                   float* q_minmax, float* k_minmax, uint8_t* send, int64_t dest_stride_bytes,
+                   void* stream) {
+    return stats_pack_common("ulp_stats_pack", 0, q, k, v, k_mean, dtype, v_scale, B, L, H, D,
+                             rank, 1, world_size, used_sequence, q_amax, k_amax, q_minmax,
+                             k_minmax, send, dest_stride_bytes, 0, stream);
+}
+
+int ulp_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
+                      const float* q_amax, const float* k_amax, int64_t B, int64_t L,
+                      int64_t H, int64_t D, int rank, int world_size, int64_t used_sequence,
+                      uint8_t* send, int64_t dest_stride_bytes, void* stream) {
+    return stats_pack_common("ulp_pack_deferred", 1, q, k, nullptr, k_mean, dtype, nullptr, B,
+                             L, H, D, rank, 1, world_size, used_sequence,
+                             const_cast<float*>(q_amax), const_cast<float*>(k_amax), nullptr,
+                             nullptr, send, dest_stride_bytes, 0, stream);
+}
+
+int ulp_group_stats_pack(const void* q, const void* k, const void* v, const void* k_mean,
+                         int dtype, const float* v_scale, int64_t B, int64_t L, int64_t H,
+                         int64_t D, int world_size, int64_t used_sequence, float* q_amax,
+                         float* k_amax, float* q_minmax, float* k_minmax, uint8_t* group,
+                         void* stream) {
+    const int64_t cb = ulp::chunk_bytes_of(B, L, H / (world_size > 0 ? world_size : 1), D);
+    return stats_pack_common("ulp_group_stats_pack", 0, q, k, v, k_mean, dtype, v_scale, B, L,
+                             H, D, 0, world_size, world_size, used_sequence, q_amax, k_amax,
+                             q_minmax, k_minmax, group, (int64_t)world_size * cb, cb, stream);
+}
+
+int ulp_group_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
+                            const float* q_amax, const float* k_amax, int64_t B, int64_t L,
+                            int64_t H, int64_t D, int world_size, int64_t used_sequence,
+                            uint8_t* group, void* stream) {
+    const int64_t cb = ulp::chunk_bytes_of(B, L, H / (world_size > 0 ? world_size : 1), D);
+    return stats_pack_common("ulp_group_pack_deferred", 1, q, k, nullptr, k_mean, dtype,
+                             nullptr, B, L, H, D, 0, world_size, world_size, used_sequence,
+                             const_cast<float*>(q_amax), const_cast<float*>(k_amax), nullptr,
+                             nullptr, group, (int64_t)world_size * cb, cb, stream);
+}
+
 int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int64_t D,
                      int world_size, int aligned, int64_t scale_sequence, int8_t* q8,
                      int8_t* k8, uint8_t* v8, float* q_scale, float* k_scale, void* stream) {

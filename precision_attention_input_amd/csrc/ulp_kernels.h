@@ -40,6 +40,20 @@ struct PackLaunch {
     int rank0, nranks, dtype;
 };
 
+// Statistics and pack from one read of the shards (phase 0), and the pack of the slots
+// whose amax derive may still change (phase 1, after derive).
+struct StatsPackLaunch {
+    const uint16_t *q, *k, *v, *mean;   // shards of rank rank0 [B, L, H, D]; mean [B, H, D]
+    const float* v_scale;               // [B, H, D] V divisor or nullptr (phase 0)
+    float *q_amax, *k_amax;             // [B, H, slots]: written by phase 0, read by phase 1
+    float *q_minmax, *k_minmax;         // [B, H, 2, 2, D] (phase 0)
+    uint8_t* send;                      // chunk (rank0 -> p) at send + p * dest_stride
+    int64_t dest_stride;
+    int64_t x_rank_stride, amax_rank_stride, minmax_rank_stride, send_rank_stride;
+    int64_t B, L, H, D, P, used;        // used = S when None
+    int rank0, nranks, dtype, phase;
+};
+
 struct UnpackLaunch {
     const uint8_t* recv;           // [P, chunk_bytes] of destination 0 of this launch
     int64_t recv_dest_stride;      // bytes between consecutive destinations' recv blocks
@@ -93,6 +107,7 @@ hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream);
 hipError_t launch_kstats(const KStatsLaunch& a, hipStream_t stream);
 hipError_t launch_derive(const DeriveLaunch& a, hipStream_t stream);
 hipError_t launch_pack(const PackLaunch& a, hipStream_t stream);
+hipError_t launch_stats_pack(const StatsPackLaunch& a, hipStream_t stream);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t stream);
 
 // Geometry shared by host and kernels.

@@ -130,3 +130,76 @@ def sub_heads(g: dict, w: W.Workload, heads: list[int]) -> dict:
         res["outs"][p] = (q8[:, :, j:j + 1], k8[:, :, j:j + 1], v8[:, :, j:j + 1],
                           qs[:, j:j + 1], ks[:, j:j + 1])
     return res
+
+
+def _poisoned_group(w: W.Workload) -> torch.Tensor:
+    """An all-to-all buffer whose every byte starts as 0x5A, so that a byte the kernels
+    leave unwritten cannot match the oracle by chance (torch.empty may hand back memory
+    that still holds an earlier run's identical bytes)."""
+    cb = ulp.chunk_bytes(w.B, w.L, w.h, w.D)
+    return torch.full((w.P, w.P, cb), 0x5A, dtype=torch.uint8, device=DEV)
+
+
+def _poisoned_stats(lead: tuple, w: W.Workload) -> tuple:
+    f = dict(dtype=torch.float32, device=DEV)
+    sl = ulp.slots(w.L)
+    return (torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f))
+
+
+def run_group_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
+    """The whole group through the one-read entry points: group_stats_pack, group_derive,
+    group_pack_deferred, group_unpack (outputs start poisoned)."""
+    P, L = w.P, w.L
+    (qa, ka, qm, km), grp = ulp.group_stats_pack(
+        dd["Q"], dd["K"], dd["V"], dd["mean"], world_size=P, used_sequence=w.used,
+        v_scale=v_scale, out=_poisoned_stats((P,), w), group=_poisoned_group(w))
+    qa_kernel, ka_kernel = qa.clone(), ka.clone()
+    ulp.group_derive(qa, ka, qm, km, dd["mean"], local_sequence=L, world_size=P)
+    ulp.group_pack_deferred(dd["Q"], dd["K"], dd["mean"], qa, ka, world_size=P, group=grp,
+                            used_sequence=w.used)
+    o = ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
+                         world_size=P, aligned=aligned, scale_sequence=w.scale_sequence)
+    torch.cuda.synchronize()
+    return dict(q_minmax=qm, k_minmax=km, q_amax_kernel=list(qa_kernel),
+                k_amax_kernel=list(ka_kernel), q_amax=list(qa), k_amax=list(ka), group=grp,
+                sends=[grp[:, r] for r in range(P)],
+                outs={p: tuple(t[p] for t in o) for p in range(P)})
+
+
+def run_per_rank_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
+    """Every rank through stats_pack, the per-rank derive and pack_deferred."""
+    P, L = w.P, w.L
+    kw = dict(world_size=P, used_sequence=w.used)
+    grp = _poisoned_group(w)
+    cb = grp.shape[-1]
+    stats = []
+    for r in range(P):
+        st, _ = ulp.stats_pack(dd["Q"][r], dd["K"][r], dd["V"][r], dd["mean"], rank=r,
+                               v_scale=v_scale, out=_poisoned_stats((), w), send=grp[0, r],
+                               dest_stride=P * cb, **kw)
+        stats.append(st)
+    q_mm = torch.stack([s[2] for s in stats])
+    k_mm = torch.stack([s[3] for s in stats])
+    qa = [s[0] for s in stats]
+    ka = [s[1] for s in stats]
+    qa_kernel = [a.clone() for a in qa]
+    ka_kernel = [a.clone() for a in ka]
+    for r in range(P):
+        ulp.derive_k_boundary_amax(qa[r], q_mm, None, rank=r, local_sequence=L, world_size=P)
+        ulp.derive_k_boundary_amax(ka[r], k_mm, dd["mean"], rank=r, local_sequence=L,
+                                   world_size=P)
+    for r in range(P):
+        ulp.pack_deferred(dd["Q"][r], dd["K"][r], dd["mean"], qa[r], ka[r], rank=r,
+                          send=grp[0, r], dest_stride=P * cb, **kw)
+    outs = {}
+    for p in range(P):
+        outs[p] = ulp.unpack_for_sage(grp[p], batch_size=w.B, local_sequence=L,
+                                      local_heads=w.h, head_dim=w.D, world_size=P,
+                                      aligned=aligned, scale_sequence=w.scale_sequence)
+    torch.cuda.synchronize()
+    return dict(q_minmax=q_mm, k_minmax=k_mm, q_amax_kernel=qa_kernel, k_amax_kernel=ka_kernel,
+                q_amax=qa, k_amax=ka, group=grp,
+                sends=[grp[:, r] for r in range(P)], outs=outs)

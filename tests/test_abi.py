@@ -132,6 +132,45 @@ def test_group_validation(L):
     assert L.ulp_group_unpack(A, 1, 100, 2, 64, 2, 1, NONE, A, A, A, A, A, None) == EINVAL
 
 
+
+def test_one_read_validation(L):
+    cb = ulp.chunk_bytes(1, 128, 2, 64)
+    # ulp_stats_pack(q, k, v, mean, dtype, v_scale, B, L, H, D, rank, P, used, qa, ka, qm, km,
+    #                send, dest_stride, stream)
+    sp = [A, A, A, A, 0, None, 1, 128, 4, 64, 0, 2, NONE, A, A, A, A, A]
+    assert L.ulp_stats_pack(*sp, cb + 16, None) == EALIGN
+    assert L.ulp_stats_pack(*sp, cb - 256, None) == EINVAL
+    bad = list(sp); bad[10] = 2                       # rank outside [0, P)
+    assert L.ulp_stats_pack(*bad, cb, None) == EINVAL and b"rank" in L.ulp_last_error()
+    bad = list(sp); bad[12] = 257                     # used_sequence > S
+    assert L.ulp_stats_pack(*bad, cb, None) == EINVAL and b"used_sequence" in L.ulp_last_error()
+    bad = list(sp); bad[2] = 0                        # v is required
+    assert L.ulp_stats_pack(*bad, cb, None) == EINVAL and b"v is NULL" in L.ulp_last_error()
+    bad = list(sp); bad[15] = A + 4                   # a min/max output misaligned
+    assert L.ulp_stats_pack(*bad, cb, None) == EALIGN
+    bad = list(sp); bad[5] = A + 8                    # optional V scale misaligned
+    assert L.ulp_stats_pack(*bad, cb, None) == EALIGN and b"v_scale" in L.ulp_last_error()
+    bad = list(sp); bad[9] = 96
+    assert L.ulp_stats_pack(*bad, cb, None) == EUNSUPPORTED
+    # ulp_pack_deferred(q, k, mean, dtype, qa, ka, B, L, H, D, rank, P, used, send, stride, s)
+    pd = [A, A, A, 0, A, A, 1, 128, 4, 64, 0, 2, NONE, A]
+    assert L.ulp_pack_deferred(*pd, cb + 256 + 16, None) == EALIGN
+    bad = list(pd); bad[2] = 0                        # k_mean is required
+    assert L.ulp_pack_deferred(*bad, cb, None) == EINVAL and b"k_mean" in L.ulp_last_error()
+    bad = list(pd); bad[11] = 3
+    assert L.ulp_pack_deferred(*bad, cb, None) == EUNSUPPORTED
+    # group forms
+    assert L.ulp_group_stats_pack(A, A, A, A, 0, None, 1, 128, 3, 64, 2, NONE, A, A, A, A, A,
+                                  None) == EINVAL          # heads not divisible by P
+    assert L.ulp_group_stats_pack(A, A, A, A, 2, None, 1, 128, 4, 64, 2, NONE, A, A, A, A, A,
+                                  None) == EINVAL          # dtype
+    assert L.ulp_group_stats_pack(A, A, A, A, 0, None, 1, 128, 4, 64, 2, 0, A, A, A, A, A,
+                                  None) == EINVAL          # used 0
+    assert L.ulp_group_pack_deferred(A, A, A, 0, A, 0, 1, 128, 4, 64, 2, NONE, A,
+                                     None) == EINVAL       # k_amax NULL
+    assert L.ulp_group_pack_deferred(A, A, A, 0, A, A, 1, 128, 4, 64, 2, NONE, A + 8,
+                                     None) == EALIGN       # group misaligned
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """The binding has no fallback: without libulp.so every call raises."""
     monkeypatch.setattr(ulp, "_lib", None)
