@@ -204,14 +204,14 @@ int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int6
  *   1. ulp_stats_pack: the grouped amax (Q raw, K centered) and the boundary min/max, as
  *      ulp_k_grouped_amax and ulp_boundary_minmax give them, and the pack of V and of every
  *      Q/K row outside the waiting slots, as ulp_pack gives it, reading each input once;
- *   2. the all-gather of the min/max and ulp_derive_k_boundary_amax, as before;
- *   3. ulp_pack_deferred: the pack of the waiting slots' Q/K rows with the derived amax
- *      (re-reads at most two groups of rows per (b, head)).
- * After step 3 the amax, min/max and chunks are bit-identical to those of ulp_k_grouped_amax
- * + ulp_boundary_minmax + derive + ulp_pack.  Arguments mean what they mean there; both
- * calls of a step take the same q, k, k_mean, used_sequence and send/group, and
- * ulp_pack_deferred the amax that derive updated in place.  The chunks are complete only
- * after step 3.
+ *   2. the all-gather of the min/max (on one GPU holding the group: nothing to do);
+ *   3. ulp_derive_pack: ulp_derive_k_boundary_amax on both amax (Q with mean +0, K with
+ *      k_mean), in place, and the pack of the waiting slots' Q/K rows with the derived
+ *      amax (it re-reads at most two groups of rows per (b, head)).
+ * After step 3 the amax, min/max and chunks are bit-identical to those of
+ * ulp_k_grouped_amax + ulp_boundary_minmax + derive + ulp_pack.  Arguments mean what they
+ * mean there; both calls of a step take the same q, k, k_mean, used_sequence and
+ * send/group.  The chunks are complete only after step 3.
  * --------------------------------------------------------------------------------- */
 
 /*   q, k, v           [B, L, H, D] dtype (rank `rank`'s shard); k_mean [B, H, D] dtype.
@@ -224,25 +224,27 @@ int ulp_stats_pack(const void* q, const void* k, const void* v, const void* k_me
                    float* q_minmax, float* k_minmax, uint8_t* send, int64_t dest_stride_bytes,
                    void* stream);
 
-/*   q_amax, k_amax    [B, H, slots(L)] float after ulp_derive_k_boundary_amax (read only). */
-int ulp_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
-                      const float* q_amax, const float* k_amax, int64_t B, int64_t L,
-                      int64_t H, int64_t D, int rank, int world_size, int64_t used_sequence,
-                      uint8_t* send, int64_t dest_stride_bytes, void* stream);
+/*   q_amax, k_amax        [B, H, slots(L)] float from ulp_stats_pack, derived in place.
+ *   q_minmax, k_minmax    gathered [P, B, H, 2, 2, D] float (every rank's min/max). */
+int ulp_derive_pack(const void* q, const void* k, const void* k_mean, int dtype, float* q_amax,
+                    float* k_amax, const float* q_minmax, const float* k_minmax, int64_t B,
+                    int64_t L, int64_t H, int64_t D, int rank, int world_size,
+                    int64_t used_sequence, uint8_t* send, int64_t dest_stride_bytes,
+                    void* stream);
 
 /* The same for every rank of a group held by one GPU: stacked shards [P, B, L, H, D],
- * q_amax, k_amax [P, B, H, slots(L)], q_minmax, k_minmax [P, B, H, 2, 2, D], and the
- * all-to-all buffer `group` laid out as for ulp_group_pack.  ulp_group_derive goes between
- * the two calls. */
+ * q_amax, k_amax [P, B, H, slots(L)], q_minmax, k_minmax [P, B, H, 2, 2, D] (written by
+ * the first call, read by the second), and the all-to-all buffer `group` laid out as for
+ * ulp_group_pack.  Two launches per step instead of the statistics, derive and pack. */
 int ulp_group_stats_pack(const void* q, const void* k, const void* v, const void* k_mean,
                          int dtype, const float* v_scale, int64_t B, int64_t L, int64_t H,
                          int64_t D, int world_size, int64_t used_sequence, float* q_amax,
                          float* k_amax, float* q_minmax, float* k_minmax, uint8_t* group,
                          void* stream);
-int ulp_group_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
-                            const float* q_amax, const float* k_amax, int64_t B, int64_t L,
-                            int64_t H, int64_t D, int world_size, int64_t used_sequence,
-                            uint8_t* group, void* stream);
+int ulp_group_derive_pack(const void* q, const void* k, const void* k_mean, int dtype,
+                          float* q_amax, float* k_amax, const float* q_minmax,
+                          const float* k_minmax, int64_t B, int64_t L, int64_t H, int64_t D,
+                          int world_size, int64_t used_sequence, uint8_t* group, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * The global K mean (the input k_mean_global of the k_grouped_amax and

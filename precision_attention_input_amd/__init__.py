@@ -22,8 +22,8 @@ __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
     "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
-    "group_stats_with_mean", "consumer_attention", "stats_pack", "pack_deferred",
-    "group_stats_pack", "group_pack_deferred",
+    "group_stats_with_mean", "consumer_attention", "stats_pack", "derive_pack",
+    "group_stats_pack", "group_derive_pack",
     "unpack_shapes",
 ]
 
@@ -77,12 +77,12 @@ def lib():
                                            vp, vp, vp, vp, vp, vp, vp], i32),
             "ulp_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i32, i64, vp,
                                 vp, vp, vp, vp, i64, vp], i32),
-            "ulp_pack_deferred": ([vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i32, i64,
-                                   vp, i64, vp], i32),
+            "ulp_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32,
+                                 i64, vp, i64, vp], i32),
             "ulp_group_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i64, vp,
                                       vp, vp, vp, vp, vp], i32),
-            "ulp_group_pack_deferred": ([vp, vp, vp, i32, vp, vp, i64, i64, i64, i64, i32, i64,
-                                         vp, vp], i32),
+            "ulp_group_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                       i64, vp, vp], i32),
             "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                         vp, vp], i32),
         }
@@ -321,8 +321,8 @@ def stats_pack(q, k, v, k_mean_global, *, rank, world_size, used_sequence=None, 
                out=None, send=None, dest_stride=None):
     """One rank's grouped amax (Q raw, K centered), boundary min/max and the pack of every
     slot that derive cannot change, from one read of q, k, v [B,L,H,D].  Returns
-    ((q_amax, k_amax, q_minmax, k_minmax), send); finish with derive_k_boundary_amax on
-    both amax and pack_deferred."""
+    ((q_amax, k_amax, q_minmax, k_minmax), send); after the all-gather of the min/max,
+    finish with derive_pack."""
     B, L, H, D = q.shape
     if out is None:
         out = _stats_out((), B, L, H, D, q.device)
@@ -340,24 +340,24 @@ def stats_pack(q, k, v, k_mean_global, *, rank, world_size, used_sequence=None, 
     return tuple(out), send
 
 
-def pack_deferred(q, k, k_mean_global, q_amax, k_amax, *, rank, world_size, send,
-                  used_sequence=None, dest_stride=None):
-    """The pack of the slots that waited for derive (q_amax, k_amax after derive)."""
-    _dev(q, k, k_mean_global, q_amax, k_amax)
+def derive_pack(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, *, rank, world_size,
+                send, used_sequence=None, dest_stride=None):
+    """derive_k_boundary_amax on both amax in place (gathered min/max [P,B,H,2,2,D]), then
+    the pack of the slots that waited for it.  Returns (q_amax, k_amax)."""
+    _dev(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax)
     B, L, H, D = q.shape
     cb = chunk_bytes(B, L, H // world_size, D)
-    _check(lib().ulp_pack_deferred(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
-                                   _p(k_amax), B, L, H, D, rank, world_size,
-                                   _none(used_sequence), _p(send), dest_stride or cb,
-                                   _stream(q)))
-    return send
+    _check(lib().ulp_derive_pack(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
+                                 _p(k_amax), _p(q_minmax), _p(k_minmax), B, L, H, D, rank,
+                                 world_size, _none(used_sequence), _p(send), dest_stride or cb,
+                                 _stream(q)))
+    return q_amax, k_amax
 
 
 def group_stats_pack(q, k, v, k_mean_global, *, world_size, used_sequence=None, v_scale=None,
                      out=None, group=None):
     """stats_pack for every rank of stacked shards [P,B,L,H,D]; returns ((q_amax, k_amax
-    [P,B,H,slots], q_minmax, k_minmax [P,B,H,2,2,D]), group).  Then group_derive and
-    group_pack_deferred."""
+    [P,B,H,slots], q_minmax, k_minmax [P,B,H,2,2,D]), group).  Then group_derive_pack."""
     P, B, L, H, D = q.shape
     if out is None:
         out = _stats_out((P,), B, L, H, D, q.device)
@@ -373,15 +373,16 @@ def group_stats_pack(q, k, v, k_mean_global, *, world_size, used_sequence=None, 
     return tuple(out), group
 
 
-def group_pack_deferred(q, k, k_mean_global, q_amax, k_amax, *, world_size, group,
-                        used_sequence=None):
-    """pack_deferred for every rank (after group_derive)."""
-    _dev(q, k, k_mean_global, q_amax, k_amax, group)
+def group_derive_pack(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, *,
+                      world_size, group, used_sequence=None):
+    """derive_pack for every rank (after group_stats_pack); returns (q_amax, k_amax)."""
+    _dev(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, group)
     P, B, L, H, D = q.shape
-    _check(lib().ulp_group_pack_deferred(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
-                                         _p(k_amax), B, L, H, D, world_size,
-                                         _none(used_sequence), _p(group), _stream(q)))
-    return group
+    _check(lib().ulp_group_derive_pack(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
+                                       _p(k_amax), _p(q_minmax), _p(k_minmax), B, L, H, D,
+                                       world_size, _none(used_sequence), _p(group),
+                                       _stream(q)))
+    return q_amax, k_amax
 
 
 # ------------------------------------------------------------------------- global K mean

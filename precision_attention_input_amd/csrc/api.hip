@@ -362,11 +362,9 @@ static int stats_pack_common(const char* fn, int phase, const void* q, const voi
     TRY(check_ptr(fn, "k_mean", k_mean));
     TRY(check_ptr(fn, "q_amax", q_amax));
     TRY(check_ptr(fn, "k_amax", k_amax));
-    if (phase == 0) {
-        TRY(check_ptr(fn, "q_minmax", q_minmax));
-        TRY(check_ptr(fn, "k_minmax", k_minmax));
-        if (v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
-    }
+    TRY(check_ptr(fn, "q_minmax", q_minmax));
+    TRY(check_ptr(fn, "k_minmax", k_minmax));
+    if (phase == 0 && v_scale) TRY(check_ptr(fn, "v_scale", v_scale));
     TRY(check_ptr(fn, "send", send));
     const int64_t cb = ulp::chunk_bytes_of(B, L, H / world_size, D);
     if (dest_stride_bytes % 256 != 0)
@@ -412,14 +410,15 @@ int ulp_stats_pack(const void* q, const void* k, const void* v, const void* k_me
                              k_minmax, send, dest_stride_bytes, 0, stream);
 }
 
-int ulp_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
-                      const float* q_amax, const float* k_amax, int64_t B, int64_t L,
-                      int64_t H, int64_t D, int rank, int world_size, int64_t used_sequence,
-                      uint8_t* send, int64_t dest_stride_bytes, void* stream) {
-    return stats_pack_common("ulp_pack_deferred", 1, q, k, nullptr, k_mean, dtype, nullptr, B,
-                             L, H, D, rank, 1, world_size, used_sequence,
-                             const_cast<float*>(q_amax), const_cast<float*>(k_amax), nullptr,
-                             nullptr, send, dest_stride_bytes, 0, stream);
+int ulp_derive_pack(const void* q, const void* k, const void* k_mean, int dtype, float* q_amax,
+                    float* k_amax, const float* q_minmax, const float* k_minmax, int64_t B,
+                    int64_t L, int64_t H, int64_t D, int rank, int world_size,
+                    int64_t used_sequence, uint8_t* send, int64_t dest_stride_bytes,
+                    void* stream) {
+    return stats_pack_common("ulp_derive_pack", 1, q, k, nullptr, k_mean, dtype, nullptr, B, L,
+                             H, D, rank, 1, world_size, used_sequence, q_amax, k_amax,
+                             const_cast<float*>(q_minmax), const_cast<float*>(k_minmax), send,
+                             dest_stride_bytes, 0, stream);
 }
 
 int ulp_group_stats_pack(const void* q, const void* k, const void* v, const void* k_mean,
@@ -433,15 +432,15 @@ int ulp_group_stats_pack(const void* q, const void* k, const void* v, const void
                              q_minmax, k_minmax, group, (int64_t)world_size * cb, cb, stream);
 }
 
-int ulp_group_pack_deferred(const void* q, const void* k, const void* k_mean, int dtype,
-                            const float* q_amax, const float* k_amax, int64_t B, int64_t L,
-                            int64_t H, int64_t D, int world_size, int64_t used_sequence,
-                            uint8_t* group, void* stream) {
+int ulp_group_derive_pack(const void* q, const void* k, const void* k_mean, int dtype,
+                          float* q_amax, float* k_amax, const float* q_minmax,
+                          const float* k_minmax, int64_t B, int64_t L, int64_t H, int64_t D,
+                          int world_size, int64_t used_sequence, uint8_t* group, void* stream) {
     const int64_t cb = ulp::chunk_bytes_of(B, L, H / (world_size > 0 ? world_size : 1), D);
-    return stats_pack_common("ulp_group_pack_deferred", 1, q, k, nullptr, k_mean, dtype,
-                             nullptr, B, L, H, D, 0, world_size, world_size, used_sequence,
-                             const_cast<float*>(q_amax), const_cast<float*>(k_amax), nullptr,
-                             nullptr, group, (int64_t)world_size * cb, cb, stream);
+    return stats_pack_common("ulp_group_derive_pack", 1, q, k, nullptr, k_mean, dtype, nullptr,
+                             B, L, H, D, 0, world_size, world_size, used_sequence, q_amax,
+                             k_amax, const_cast<float*>(q_minmax), const_cast<float*>(k_minmax),
+                             group, (int64_t)world_size * cb, cb, stream);
 }
 
 int ulp_group_unpack(const uint8_t* group, int64_t B, int64_t L, int64_t h, int64_t D,

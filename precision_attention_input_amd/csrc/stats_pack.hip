@@ -9,7 +9,7 @@
 // other slot's amax is final once this rank has seen the group's rows.
 //
 // Phase 0: one 256-thread workgroup per (rank, b, slot, 128 channels: one head at D = 128,
-// two at D = 64) loads the rank's rows of the group (at most 64, two per thread) of Q, K
+// two at D = 64) loads the rank's rows of the group (at most 64, four per thread) of Q, K
 // and V once, converts V to E4M3 at once, reduces the raw |Q| and centered |K - mean| amax
 // of each head (and, for the first and last slot, the per-channel raw min/max) in the
 // same registers, writes them, and quantizes Q and K with the new scales, unless the slot
@@ -32,6 +32,7 @@ struct StatsPackParams {
     float *q_amax, *k_amax, *q_minmax, *k_minmax;
     uint8_t* send;
     int64_t dest_stride, x_rank_stride, amax_rank_stride, minmax_rank_stride, send_rank_stride;
+    int64_t gathered_stride;    // phase 1: floats between ranks of the gathered min/max
     int64_t B, L, H, h, P, S, used, slots, sec, ssec;
     int rank0, nhb, grid_slots;
 };
@@ -95,10 +96,10 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
     const int64_t n = last_group(rank, L) - g0 + 1;
     int64_t j = jg;
     if (PHASE == 1) {
-        if (jg == 1 && n == 1) return;
+        if (jg == 1 && n == 1) return;   // one touched slot: the jg = 0 workgroup has it
         j = jg == 0 ? 0 : n - 1;
-        if (!waits_for_derive(rank, L, p.S, p.used, j, n)) return;
     }
+    const bool wait = waits_for_derive(rank, L, p.S, p.used, j, n);
     const int64_t arank = rz * p.amax_rank_stride;
 
     if (PHASE == 0 && j >= n) {
@@ -140,15 +141,17 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
     const int64_t xs = H * D;                              // row stride of the shards
     const uint64_t x0 = (uint64_t)rz * p.x_rank_stride +
                         (uint64_t)(((b * L + l0) * H + head) * D + pc * 8);
-    uint4 qv[4], kv[4], vv[4];
+    uint4 qv[4], kv[4], vv[4], m;
+    if (PHASE == 0 || wait) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint64_t o = x0 + (uint64_t)(min(rq + 16 * i, nrow - 1) * xs);
-        qv[i] = load16(p.q + o);
-        kv[i] = load16(p.k + o);
-        if constexpr (PHASE == 0) vv[i] = load16<true>(p.v + o);
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t o = x0 + (uint64_t)(min(rq + 16 * i, nrow - 1) * xs);
+            qv[i] = load16(p.q + o);
+            kv[i] = load16(p.k + o);
+            if constexpr (PHASE == 0) vv[i] = load16<true>(p.v + o);
+        }
+        m = load16(p.mean + (b * H + head) * D + pc * 8);
     }
-    const uint4 m = load16(p.mean + (b * H + head) * D + pc * 8);
     float4 sv[4];
     if constexpr (PHASE == 0 && VS) {
         // the 8 channels' V divisors, twice (the conversion takes two rows of 8 channels)
@@ -261,10 +264,42 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
                 __syncthreads();
             }
         }
-        if (waits_for_derive(rank, L, p.S, p.used, j, n)) return;
+        if (wait) return;
     } else {
-        qamax = p.q_amax[arank + (b * H + head) * p.slots + j];
-        kamax = p.k_amax[arank + (b * H + head) * p.slots + j];
+        // derive_k_boundary_amax (description) for this slot, both tensors, every head of
+        // the block: the max over the ranks touching the group of max(1e-7, max_d
+        // max(RN(max - m), RN(m - min))) of their gathered min/max (m = +0 for Q).  Thread
+        // (tensor t, channel c) first takes its channel's max over the touching ranks; the
+        // max over channels and the floor follow (max is exact and order-free, so this is
+        // the same value).
+        const int t = tid >> 7, cc = tid & 127, hd = cc / D, d = cc % D;
+        const int64_t dhead = (int64_t)hb * HPB + hd;
+        const float mref =
+            t ? decode1<DT>(p.mean[(b * H + dhead) * D + d]) : 0.0f;
+        const float* mm = t ? p.k_minmax : p.q_minmax;
+        float v = -__builtin_inff();
+        for (int64_t r = 0; r < p.P; ++r) {
+            if (!(r * L < kGroup * g + kGroup && kGroup * g < r * L + L)) continue;
+            const int er = g == first_group(r, L) ? 0 : 1;
+            const float* base = mm + r * p.gathered_stride + (((b * H + dhead) * 2 + er) * 2) * D;
+            v = fmaxf(v, fmaxf(base[D + d] - mref, mref - base[d]));
+        }
+        v = wave_max_xor<63>(v);
+        __shared__ float dred[4];
+        if (lane == 0) dred[wave] = v;
+        __syncthreads();
+        // wave w holds channels [64 (w & 1), 64 (w & 1) + 64) of tensor w >> 1
+        const float qd = D == 128 ? fmaxf(dred[0], dred[1]) : dred[hib];
+        const float kd = D == 128 ? fmaxf(dred[2], dred[3]) : dred[2 + hib];
+        qamax = fmaxf(kFloor, qd);
+        kamax = fmaxf(kFloor, kd);
+        if (tid < 2 * HPB) {
+            const int tt = tid / HPB, hh = tid % HPB;
+            const float a = fmaxf(kFloor, D == 128 ? fmaxf(dred[2 * tt], dred[2 * tt + 1])
+                                                   : dred[2 * tt + hh]);
+            (tt ? p.k_amax : p.q_amax)[arank + (b * H + (int64_t)hb * HPB + hh) * p.slots + j] = a;
+        }
+        if (!wait) return;
     }
 
     // Quantize every row of the rank in the group (rows in the zero tail included), two
@@ -311,6 +346,7 @@ hipError_t launch_t(const StatsPackLaunch& a, hipStream_t stream) {
     p.amax_rank_stride = a.amax_rank_stride;
     p.minmax_rank_stride = a.minmax_rank_stride;
     p.send_rank_stride = a.send_rank_stride;
+    p.gathered_stride = a.B * a.H * 4 * D;
     p.B = a.B;
     p.L = a.L;
     p.H = a.H;

@@ -150,16 +150,15 @@ def _poisoned_stats(lead: tuple, w: W.Workload) -> tuple:
 
 
 def run_group_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
-    """The whole group through the one-read entry points: group_stats_pack, group_derive,
-    group_pack_deferred, group_unpack (outputs start poisoned)."""
+    """The whole group through the one-read entry points: group_stats_pack,
+    group_derive_pack, group_unpack (outputs start poisoned)."""
     P, L = w.P, w.L
     (qa, ka, qm, km), grp = ulp.group_stats_pack(
         dd["Q"], dd["K"], dd["V"], dd["mean"], world_size=P, used_sequence=w.used,
         v_scale=v_scale, out=_poisoned_stats((P,), w), group=_poisoned_group(w))
     qa_kernel, ka_kernel = qa.clone(), ka.clone()
-    ulp.group_derive(qa, ka, qm, km, dd["mean"], local_sequence=L, world_size=P)
-    ulp.group_pack_deferred(dd["Q"], dd["K"], dd["mean"], qa, ka, world_size=P, group=grp,
-                            used_sequence=w.used)
+    ulp.group_derive_pack(dd["Q"], dd["K"], dd["mean"], qa, ka, qm, km, world_size=P,
+                          group=grp, used_sequence=w.used)
     o = ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
                          world_size=P, aligned=aligned, scale_sequence=w.scale_sequence)
     torch.cuda.synchronize()
@@ -170,7 +169,7 @@ def run_group_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> d
 
 
 def run_per_rank_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
-    """Every rank through stats_pack, the per-rank derive and pack_deferred."""
+    """Every rank through stats_pack, then (after the min/max are gathered) derive_pack."""
     P, L = w.P, w.L
     kw = dict(world_size=P, used_sequence=w.used)
     grp = _poisoned_group(w)
@@ -188,12 +187,8 @@ def run_per_rank_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -
     qa_kernel = [a.clone() for a in qa]
     ka_kernel = [a.clone() for a in ka]
     for r in range(P):
-        ulp.derive_k_boundary_amax(qa[r], q_mm, None, rank=r, local_sequence=L, world_size=P)
-        ulp.derive_k_boundary_amax(ka[r], k_mm, dd["mean"], rank=r, local_sequence=L,
-                                   world_size=P)
-    for r in range(P):
-        ulp.pack_deferred(dd["Q"][r], dd["K"][r], dd["mean"], qa[r], ka[r], rank=r,
-                          send=grp[0, r], dest_stride=P * cb, **kw)
+        ulp.derive_pack(dd["Q"][r], dd["K"][r], dd["mean"], qa[r], ka[r], q_mm, k_mm, rank=r,
+                        send=grp[0, r], dest_stride=P * cb, **kw)
     outs = {}
     for p in range(P):
         outs[p] = ulp.unpack_for_sage(grp[p], batch_size=w.B, local_sequence=L,

@@ -152,13 +152,16 @@ def test_one_read_validation(L):
     assert L.ulp_stats_pack(*bad, cb, None) == EALIGN and b"v_scale" in L.ulp_last_error()
     bad = list(sp); bad[9] = 96
     assert L.ulp_stats_pack(*bad, cb, None) == EUNSUPPORTED
-    # ulp_pack_deferred(q, k, mean, dtype, qa, ka, B, L, H, D, rank, P, used, send, stride, s)
-    pd = [A, A, A, 0, A, A, 1, 128, 4, 64, 0, 2, NONE, A]
-    assert L.ulp_pack_deferred(*pd, cb + 256 + 16, None) == EALIGN
+    # ulp_derive_pack(q, k, mean, dtype, qa, ka, qm, km, B, L, H, D, rank, P, used, send,
+    #                 stride, stream)
+    pd = [A, A, A, 0, A, A, A, A, 1, 128, 4, 64, 0, 2, NONE, A]
+    assert L.ulp_derive_pack(*pd, cb + 256 + 16, None) == EALIGN
     bad = list(pd); bad[2] = 0                        # k_mean is required
-    assert L.ulp_pack_deferred(*bad, cb, None) == EINVAL and b"k_mean" in L.ulp_last_error()
-    bad = list(pd); bad[11] = 3
-    assert L.ulp_pack_deferred(*bad, cb, None) == EUNSUPPORTED
+    assert L.ulp_derive_pack(*bad, cb, None) == EINVAL and b"k_mean" in L.ulp_last_error()
+    bad = list(pd); bad[7] = 0                        # the gathered K min/max is required
+    assert L.ulp_derive_pack(*bad, cb, None) == EINVAL and b"k_minmax" in L.ulp_last_error()
+    bad = list(pd); bad[13] = 3
+    assert L.ulp_derive_pack(*bad, cb, None) == EUNSUPPORTED
     # group forms
     assert L.ulp_group_stats_pack(A, A, A, A, 0, None, 1, 128, 3, 64, 2, NONE, A, A, A, A, A,
                                   None) == EINVAL          # heads not divisible by P
@@ -166,10 +169,11 @@ def test_one_read_validation(L):
                                   None) == EINVAL          # dtype
     assert L.ulp_group_stats_pack(A, A, A, A, 0, None, 1, 128, 4, 64, 2, 0, A, A, A, A, A,
                                   None) == EINVAL          # used 0
-    assert L.ulp_group_pack_deferred(A, A, A, 0, A, 0, 1, 128, 4, 64, 2, NONE, A,
-                                     None) == EINVAL       # k_amax NULL
-    assert L.ulp_group_pack_deferred(A, A, A, 0, A, A, 1, 128, 4, 64, 2, NONE, A + 8,
-                                     None) == EALIGN       # group misaligned
+    assert L.ulp_group_derive_pack(A, A, A, 0, A, 0, A, A, 1, 128, 4, 64, 2, NONE, A,
+                                   None) == EINVAL         # k_amax NULL
+    assert L.ulp_group_derive_pack(A, A, A, 0, A, A, A, A, 1, 128, 4, 64, 2, NONE, A + 8,
+                                   None) == EALIGN         # group misaligned
+
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """The binding has no fallback: without libulp.so every call raises."""

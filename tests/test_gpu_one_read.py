@@ -1,5 +1,5 @@
-"""The one-read step (statistics and pack from one read of Q, K and V, then derive, then the
-pack of the slots that waited for derive) against the CPU oracle, bit for bit (GPU).
+"""The one-read step (statistics and pack from one read of Q, K and V, then derive together
+with the pack of the slots that waited for it) against the CPU oracle, bit for bit (GPU).
 
 The oracle runs the step as the pages lay it out (grouped amax, boundary min/max, derive,
 pack); the one-read entry points must reproduce every intermediate (kernel amax, min/max,
@@ -133,9 +133,8 @@ def test_one_read_writes_nothing_outside(olib):
     (qa, ka, qm, km), grp = ulp.group_stats_pack(
         dd["Q"], dd["K"], dd["V"], dd["mean"], world_size=P, used_sequence=w.used,
         out=tuple(b[1] for b in bufs[:4]), group=bufs[4][1])
-    ulp.group_derive(qa, ka, qm, km, dd["mean"], local_sequence=L, world_size=P)
-    ulp.group_pack_deferred(dd["Q"], dd["K"], dd["mean"], qa, ka, world_size=P, group=grp,
-                            used_sequence=w.used)
+    ulp.group_derive_pack(dd["Q"], dd["K"], dd["mean"], qa, ka, qm, km, world_size=P,
+                          group=grp, used_sequence=w.used)
     torch.cuda.synchronize()
     for i, (buf, _) in enumerate(bufs):
         m = torch.cat([buf[:4096], buf[-4096:]])
