@@ -373,7 +373,8 @@ static int stats_pack_common(const char* fn, int phase, const void* q, const voi
     if (dest_stride_bytes < cb)
         return fail(ULP_EINVAL, "%s: dest_stride_bytes %lld is smaller than the chunk (%lld)",
                     fn, (long long)dest_stride_bytes, (long long)cb);
-    if (B * ulp::slots_of(L) * (H * D / 128) >= kMaxGrid)
+    if (B * ulp::slots_of(L) * (H * D / 128) + B * ((L + 7) / 8) * ((H * D + 511) / 512) >=
+        kMaxGrid)
         return fail(ULP_EINVAL, "%s: problem too large for one launch", fn);
     ulp::StatsPackLaunch a{};
     a.q = static_cast<const uint16_t*>(q);

@@ -9,15 +9,18 @@
 // other slot's amax is final once this rank has seen the group's rows.
 //
 // Phase 0: one 256-thread workgroup per (rank, b, slot, 128 channels: one head at D = 128,
-// two at D = 64) loads the rank's rows of the group (at most 64, four per thread) of Q, K
-// and V once, converts V to E4M3 at once, reduces the raw |Q| and centered |K - mean| amax
-// of each head (and, for the first and last slot, the per-channel raw min/max) in the
-// same registers, writes them, and quantizes Q and K with the new scales, unless the slot
-// must wait for derive.  Phase 1, after derive: one workgroup per (rank, b, first or last
-// slot, 128 channels) re-reads the rows of the slots that waited and quantizes them with
-// the derived amax.  Together with derive in between, the outputs are bit-identical to
-// the separate statistics, derive and pack launches: the same amax (a direct max of the
-// same |RN(x - mean)| values, which the min/max identity of derive_k_boundary_amax equals
+// two at D = 64) loads the rank's rows of the group (at most 64, four per thread) of Q and
+// K once, reduces the raw |Q| and centered |K - mean| amax of each head (and, for the first
+// and last slot, the per-channel raw min/max) in the same registers, writes them, and
+// quantizes Q and K with the new scales, unless the slot must wait for derive.  V, which
+// needs no statistic, is converted in the same launch: by the same workgroups from their
+// own rows when the launch's data fits the cache, by workgroups of its own in the pack
+// kernel's layout when it streams from HBM.  Phase 1, after the min/max are gathered: one
+// workgroup per (rank, b, first or last slot, 128 channels) derives the slot's amax for Q
+// and K as derive_k_boundary_amax (description) does, writes it, and, if the slot waited,
+// re-reads its rows and quantizes them with it.  The outputs are bit-identical to the
+// separate statistics, derive and pack launches: the same amax (a direct max of the same
+// |RN(x - mean)| values, which the min/max identity of derive_k_boundary_amax equals
 // exactly), the same chunk bytes.
 #include "pack_device.h"
 #include "ulp_kernels.h"
@@ -35,6 +38,7 @@ struct StatsPackParams {
     int64_t gathered_stride;    // phase 1: floats between ranks of the gathered min/max
     int64_t B, L, H, h, P, S, used, slots, sec, ssec;
     int rank0, nhb, grid_slots;
+    int n_qk, v_row_blocks, v_col_blocks;   // phase 0: V workgroups follow the n_qk others
 };
 
 // Whether slot j of a rank with n touched slots must be quantized after derive (above).
@@ -84,6 +88,43 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
             const int64_t end = sect < 3 ? (sect + 1) * p.sec : 3 * p.sec + (sect - 2) * p.ssec;
             if (start + off < end) send[dst * p.dest_stride + start + off] = 0;
         }
+    }
+
+    // Where the launch streams from HBM, V goes through workgroups of its own (after the
+    // statistics workgroups) in the pack kernel's layout; in smaller launches, whose data
+    // the cache holds, the statistics workgroups convert it with their own rows.  Each
+    // choice measured 2-8 % faster than the other at its sizes.
+    constexpr bool V_SPLIT = NT;
+    constexpr bool V_HERE = PHASE == 0 && !V_SPLIT;
+    if (PHASE == 0 && V_SPLIT && (int)blockIdx.x >= p.n_qk) {
+        // V needs no statistic: the pack kernel's layout, 8 rows x 32 sixteen-element
+        // vectors per workgroup, column blocks fastest (whole rows in flight).
+        constexpr int VPH = D / 16;
+        const uint32_t vbid = blockIdx.x - (uint32_t)p.n_qk;
+        const uint32_t cblk = vbid % (uint32_t)p.v_col_blocks;
+        const uint32_t rblk = vbid / (uint32_t)p.v_col_blocks;
+        const uint32_t bb = rblk / (uint32_t)p.v_row_blocks;
+        const uint32_t l = (rblk % (uint32_t)p.v_row_blocks) * 8 + tid / 32;
+        const uint32_t col = cblk * 32 + tid % 32;
+        if (l >= (uint32_t)L || col >= (uint32_t)(H * VPH)) return;
+        const uint32_t vhead = col / VPH, vdv = col % VPH;
+        const uint64_t xo = (uint64_t)rz * p.x_rank_stride +
+                            ((uint64_t)bb * L + l) * (uint64_t)(H * D) + col * 16;
+        const uint4 v0 = load16<true>(p.v + xo);
+        const uint4 v1 = load16<true>(p.v + xo + 8);
+        uint8_t* o = send + (int64_t)(vhead / h) * p.dest_stride + 2 * p.sec +
+                     (((int64_t)bb * L + l) * h + vhead % h) * D + vdv * 16;
+        if constexpr (VS) {
+            const float4* vp = reinterpret_cast<const float4*>(
+                p.v_scale + ((int64_t)bb * H + vhead) * D + vdv * 16);
+            float4 sv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = vp[i];
+            store16<NT>(o, e4m3x16_scaled<DT>(v0, v1, sv));
+        } else {
+            store16<NT>(o, e4m3x16<DT>(v0, v1));
+        }
+        return;
     }
 
     // Workgroup: head block fastest, so the workgroups in flight cover whole rows.
@@ -148,12 +189,12 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
             const uint64_t o = x0 + (uint64_t)(min(rq + 16 * i, nrow - 1) * xs);
             qv[i] = load16(p.q + o);
             kv[i] = load16(p.k + o);
-            if constexpr (PHASE == 0) vv[i] = load16<true>(p.v + o);
+            if constexpr (V_HERE) vv[i] = load16<true>(p.v + o);
         }
         m = load16(p.mean + (b * H + head) * D + pc * 8);
     }
     float4 sv[4];
-    if constexpr (PHASE == 0 && VS) {
+    if constexpr (V_HERE && VS) {
         // the 8 channels' V divisors, twice (the conversion takes two rows of 8 channels)
         const float4* vp =
             reinterpret_cast<const float4*>(p.v_scale + (b * H + head) * D + pc * 8);
@@ -171,18 +212,20 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
 
     float qamax, kamax;
     if constexpr (PHASE == 0) {
-        // V needs no statistic: convert and store it first, which frees its registers.
-        // Each conversion takes two rows of this thread's 8 channels.
+        if constexpr (V_HERE) {
+            // V needs no statistic: convert and store it first, which frees its registers.
+            // Each conversion takes two rows of this thread's 8 channels.
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-            uint4 e;
-            if constexpr (VS)
-                e = e4m3x16_scaled<DT>(vv[i], vv[i + 1], sv);
-            else
-                e = e4m3x16<DT>(vv[i], vv[i + 1]);
-            if (rq + 16 * i < nrow) store8<NT>(out0 + 2 * p.sec + (rq + 16 * i) * os, e.x, e.y);
-            if (rq + 16 * i + 16 < nrow)
-                store8<NT>(out0 + 2 * p.sec + (rq + 16 * i + 16) * os, e.z, e.w);
+            for (int i = 0; i < 4; i += 2) {
+                uint4 e;
+                if constexpr (VS)
+                    e = e4m3x16_scaled<DT>(vv[i], vv[i + 1], sv);
+                else
+                    e = e4m3x16<DT>(vv[i], vv[i + 1]);
+                uint8_t* o = out0 + 2 * p.sec + (rq + 16 * i) * os;
+                if (rq + 16 * i < nrow) store8<NT>(o, e.x, e.y);
+                if (rq + 16 * i + 16 < nrow) store8<NT>(o + 16 * os, e.z, e.w);
+            }
         }
 
         // Amax of this thread's rows, |fp32(q)| and |RN(fp32(k) - fp32(mean))| (>= 0, so an
@@ -360,11 +403,16 @@ hipError_t launch_t(const StatsPackLaunch& a, hipStream_t stream) {
     p.rank0 = a.rank0;
     p.nhb = (int)(a.H * D / 128);
     p.grid_slots = PHASE == 0 ? (int)p.slots : 2;
-    const dim3 grid((unsigned)(a.B * p.grid_slots * p.nhb), 1, (unsigned)a.nranks);
+    p.n_qk = (int)(a.B * p.grid_slots * p.nhb);
+    p.v_row_blocks = (int)((a.L + 7) / 8);
+    p.v_col_blocks = (int)((a.H * D / 16 + 31) / 32);
     const dim3 block(kThreads);
     if constexpr (PHASE == 0) {
         const int64_t written = a.nranks * 3 * a.B * a.L * a.H * D;   // code bytes
         const bool nt = written > kResidentBytes;
+        // V workgroups of their own in the streaming instantiation (see the kernel)
+        const int64_t n_v = nt ? a.B * p.v_row_blocks * p.v_col_blocks : 0;
+        const dim3 grid((unsigned)(p.n_qk + n_v), 1, (unsigned)a.nranks);
         if (a.v_scale) {
             if (nt) hipLaunchKernelGGL((stats_pack_kernel<DT, D, 0, true, true>), grid, block, 0, stream, p);
             else hipLaunchKernelGGL((stats_pack_kernel<DT, D, 0, false, true>), grid, block, 0, stream, p);
@@ -373,6 +421,7 @@ hipError_t launch_t(const StatsPackLaunch& a, hipStream_t stream) {
             else hipLaunchKernelGGL((stats_pack_kernel<DT, D, 0, false, false>), grid, block, 0, stream, p);
         }
     } else {
+        const dim3 grid((unsigned)p.n_qk, 1, (unsigned)a.nranks);
         hipLaunchKernelGGL((stats_pack_kernel<DT, D, 1, false, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();

@@ -113,6 +113,22 @@ def test_v_scale_one_read(olib, wname):
                 "one-read per-rank v_scale")
 
 
+
+def test_v_scale_one_read_streaming_launch(olib):
+    """The long workload (its launch streams from HBM, so V goes through workgroups of its
+    own) with the caller's V scale: every byte of the all-to-all buffer equals the separate
+    pack's, which the V-scale tests check against the oracle."""
+    w = W.LONG_UNALIGNED
+    say(f"[one-read v_scale] {w.name}")
+    d = W.generate(w)
+    vsd = W.v_scale(w).to(DEV)
+    dd = to_dev(d, w.P)
+    f = run_group_one_read(w, dd, aligned=w.aligned, v_scale=vsd)
+    g = run_group(w, dd, aligned=w.aligned, v_scale=vsd)
+    assert_bits_equal(f["group"], g["group"], "all-to-all buffer")
+    del dd, f, g
+    torch.cuda.empty_cache()
+
 def test_one_read_writes_nothing_outside(olib):
     """Outputs inside canary-filled buffers: nothing is written past them."""
     w = small(B=2, P=4, L=100, H=8, D=64, dtype=torch.float16, used=350, seed=8)
