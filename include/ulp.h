@@ -22,8 +22,11 @@
  *    asynchronous on that stream and never synchronize the host.
  *  - The library allocates no device memory and keeps no state between calls except a
  *    thread-local error message.  The caller owns every buffer.
- *  - Outputs must not alias inputs (except the in-place amax of the derive call).
- *  - Every output byte is written by every call, including unused slots and padding.
+ *  - Outputs must not alias inputs (except the amax that the derive calls update in
+ *    place: ulp_derive_k_boundary_amax, ulp_group_derive, ulp_derive_pack,
+ *    ulp_group_derive_pack).
+ *  - Every output byte is written by every call, including unused slots and padding (the
+ *    chunks of the one-read pair ulp_stats_pack + ulp_derive_pack: by the two together).
  *  - Return value: ULP_OK, or an error code with NOTHING launched and nothing written;
  *    ulp_last_error() then describes the problem.  ULP_ELAUNCH reports a HIP launch error.
  *  - Zero-filling of rows >= used_sequence in Q, K and V is a caller contract
