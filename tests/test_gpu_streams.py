@@ -55,15 +55,24 @@ def _alloc(w):
     return st, grp, out, (kmf, kmd), ws
 
 
-def _step(w, src, bufs):
-    """K mean -> statistics -> derive -> pack -> unpack, all on the current stream."""
+def _step(w, src, bufs, one_read=False):
+    """K mean -> statistics -> derive -> pack -> unpack, all on the current stream (with
+    one_read: K mean -> statistics and pack -> derive and the waiting slots' pack ->
+    unpack)."""
     st, grp, out, km, ws = bufs
     P, L = w.P, w.L
     ulp.k_mean(src["K"], world_size=P, used_sequence=w.used, workspace=ws, out=km)
-    qa, ka, qm, km_ = ulp.group_stats(src["Q"], src["K"], km[1], world_size=P,
-                                      used_sequence=w.used, out=st)
-    ulp.group_derive(qa, ka, qm, km_, km[1], local_sequence=L, world_size=P)
-    ulp.group_pack(src["Q"], src["K"], src["V"], km[1], qa, ka, world_size=P, group=grp)
+    if one_read:
+        (qa, ka, qm, km_), _ = ulp.group_stats_pack(src["Q"], src["K"], src["V"], km[1],
+                                                    world_size=P, used_sequence=w.used,
+                                                    out=st, group=grp)
+        ulp.group_derive_pack(src["Q"], src["K"], km[1], qa, ka, qm, km_, world_size=P,
+                              group=grp, used_sequence=w.used)
+    else:
+        qa, ka, qm, km_ = ulp.group_stats(src["Q"], src["K"], km[1], world_size=P,
+                                          used_sequence=w.used, out=st)
+        ulp.group_derive(qa, ka, qm, km_, km[1], local_sequence=L, world_size=P)
+        ulp.group_pack(src["Q"], src["K"], src["V"], km[1], qa, ka, world_size=P, group=grp)
     ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
                      world_size=P, aligned=w.aligned, scale_sequence=w.scale_sequence,
                      out=out)
@@ -73,7 +82,8 @@ def _step(w, src, bufs):
                                              dtype=torch.float16, used=350,
                                              scale_sequence=350, seed=31)],
                          ids=["tiny", "b2_p4_l100_fp16_u350"])
-def test_pipeline_in_a_hip_graph(olib, w):
+@pytest.mark.parametrize("one_read", [False, True], ids=["separate", "one_read"])
+def test_pipeline_in_a_hip_graph(olib, w, one_read):
     """Captured once, replayed on three different inputs copied into the captured buffers;
     every replay matches the oracle run on the same inputs (the mean included: it is formed
     inside the graph by ulp_k_mean and compared with the oracle's)."""
@@ -90,19 +100,19 @@ def test_pipeline_in_a_hip_graph(olib, w):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):            # warm-up outside the capture
-        _step(w, src, bufs)
+        _step(w, src, bufs, one_read)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _step(w, src, bufs)
+        _step(w, src, bufs, one_read)
     torch.cuda.synchronize()
     for i, d in enumerate(inputs):
         load(d)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        say(f"[graph] {w.name} replay {i}")
+        say(f"[graph] {w.name} one_read={one_read} replay {i}")
         st, grp, out, km, ws = bufs
         # the mean formed inside the graph: the oracle's within its tolerance, and the
         # input of the oracle run below (k_mean_global is an input of the path)
@@ -114,5 +124,9 @@ def test_pipeline_in_a_hip_graph(olib, w):
         for p in range(w.P):
             for k, name in enumerate(("q8", "k8", "v8", "q_scale", "k_scale")):
                 assert_bits_equal(out[k][p], ref["outs"][p][k], f"replay {i}: {name} dest {p}")
+        for r in range(w.P):
+            assert_bits_equal(st[0][r], ref["q_amax"][r], f"replay {i}: derived q_amax r{r}")
+            assert_bits_equal(st[1][r], ref["k_amax"][r], f"replay {i}: derived k_amax r{r}")
+            assert_bits_equal(grp[:, r], ref["sends"][r], f"replay {i}: chunks of rank {r}")
         # eager work between replays must not disturb the graph's buffers
         _ = (src["Q"].float() * 2).sum().item()
