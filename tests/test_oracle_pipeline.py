@@ -143,6 +143,40 @@ def test_derive_bit_neutral_on_non_crossing_and_identical_on_touchers(olib):
                 assert torch.equal(res["k_amax"][r][..., j], res["k_amax_kernel"][r][..., j])
 
 
+
+def _waits_for_derive(r, L, S, used, j, n):
+    """The slots the one-read pack leaves for after derive: a rank's first or last slot whose
+    group another rank also touches or whose rows all lie in the zero tail."""
+    if j not in (0, n - 1):
+        return False
+    g = first_group(r, L) + j
+    lo, hi = max(64 * g, r * L), min(64 * g + 64, r * L + L)
+    shared = 64 * g < r * L or min(64 * g + 64, S) > hi
+    return shared or min(hi, used) <= lo
+
+
+def test_derive_changes_only_slots_that_wait(olib):
+    """The premise of packing from one read (statistics and pack in one pass, then derive
+    and the pack of the waiting slots): on every enumerated shape, derive (derive page,
+    description) leaves every slot outside the waiting set bit for bit as the grouped amax
+    wrote it, for Q and for K; and the waiting set is not vacuous (derive does change some
+    of its slots: crossing groups and boundary groups in the zero tail)."""
+    changed_waiting = 0
+    for w in ENUM[::3]:
+        d, res, _ = run(w)
+        S, used = w.S, w.used or w.S
+        for r in range(w.P):
+            n = last_group(r, w.L) - first_group(r, w.L) + 1
+            for t in ("q", "k"):
+                before, after = res[f"{t}_amax_kernel"][r], res[f"{t}_amax"][r]
+                for j in range(before.shape[-1]):
+                    same = torch.equal(before[..., j], after[..., j])
+                    if j >= n or not _waits_for_derive(r, w.L, S, used, j, n):
+                        assert same, (w.name, w.used, r, t, j)
+                    elif not same:
+                        changed_waiting += 1
+    assert changed_waiting > 0
+
 def test_scale_sequence_outputs_are_prefix_of_full_width(olib):
     """unpack_for_sage description: scales at scale_sequence are byte-identical to the
     leading slots of the full-width tensors; Q/K/V stay full length."""
