@@ -15,7 +15,10 @@ derive_ms; the roofline figure uses pack_ms), and K back-to-back pack+unpack pai
 the reported value: pack+unpack algorithmic bytes / average pair time.  Each of these
 per-kernel loops is preceded by three untimed calls and timed five times; the median loop
 is reported.  The global K mean
-(an input of the step) is timed the same way, as k_mean GB/s.  Prints one JSON line.
+(an input of the step) is timed the same way, as k_mean GB/s.  The same step with the
+statistics and the pack from one read of Q, K and V (two launches before the unpack instead
+of three; same outputs) is timed likewise and reported as one_read_step_ms.  Prints one
+JSON line.
 """
 from __future__ import annotations
 
