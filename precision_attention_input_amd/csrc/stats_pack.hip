@@ -176,9 +176,9 @@ __global__ __launch_bounds__(kThreads) void stats_pack_kernel(StatsPackParams p)
     const int namax = (int)(amax_hi - lo);                 // may be <= 0
     const int64_t l0 = lo - rank * L;                      // local row of the first row
 
-    // Issue every load first: four rows of Q, K (and V in phase 0), 16 bytes each, and the
-    // K mean.  Rows past the range re-read the last row (no load sits in a branch, so all
-    // are in flight together).
+    // Issue every load first: four rows of Q and K (and of V where these workgroups convert
+    // it), 16 bytes each, and the K mean.  Rows past the range re-read the last row (no load
+    // sits in a branch, so all are in flight together).
     const int64_t xs = H * D;                              // row stride of the shards
     const uint64_t x0 = (uint64_t)rz * p.x_rank_stride +
                         (uint64_t)(((b * L + l0) * H + head) * D + pc * 8);
