@@ -41,6 +41,24 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+
+def test_binding_signatures_match_header(L):
+    """Every declaration in include/ulp.h has a binding with the same number of arguments,
+    pointers where the header has pointers, int64_t and int where it has those (a drifted
+    signature would otherwise pass garbage to a kernel)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"\b(?:int64_t|int|const char\*)\s+(ulp_\w+)\s*\(([^)]*)\)\s*;", text)
+    assert len(decls) == len(declared())
+    for name, params in decls:
+        want = []
+        for prm in (x.strip() for x in params.split(",")):
+            if not prm or prm == "void":
+                continue
+            want.append(ctypes.c_void_p if "*" in prm else
+                        ctypes.c_int64 if prm.startswith("int64_t") else ctypes.c_int)
+        got = list(getattr(L, name).argtypes or [])
+        assert got == want, f"{name}: binding {got} vs header {want}"
+
 def test_geometry_helpers_match_oracle(L, olib):
     for Lseq in [1, 2, 31, 63, 64, 65, 96, 100, 127, 128, 129, 200, 1000, 2048, 4096, 9360]:
         assert ulp.slots(Lseq) == oracle.slots(Lseq)
