@@ -42,6 +42,21 @@ def test_every_declared_symbol_is_exported(L):
 
 
 
+
+def test_library_exports_nothing_undeclared(L):
+    """The C-ABI surface is exactly ulp.h: no ulp_* symbol is exported that the header does
+    not declare (read with nm from the library built here)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", ulp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {f[2] for f in (line.split() for line in out.splitlines())
+                if len(f) == 3 and f[1] == "T" and f[2].startswith("ulp_")}
+    assert exported == set(declared())
+
 def test_binding_signatures_match_header(L):
     """Every declaration in include/ulp.h has a binding with the same number of arguments,
     pointers where the header has pointers, int64_t and int where it has those (a drifted
