@@ -27,8 +27,13 @@
  *    ulp_group_derive_pack).
  *  - Every output byte is written by every call, including unused slots and padding (the
  *    chunks of the one-read pair ulp_stats_pack + ulp_derive_pack: by the two together).
- *  - Return value: ULP_OK, or an error code with NOTHING launched and nothing written;
- *    ulp_last_error() then describes the problem.  ULP_ELAUNCH reports a HIP launch error.
+ *  - Return value: ULP_OK or an error code; ulp_last_error() then describes the problem.
+ *    Argument errors (ULP_EINVAL, ULP_EUNSUPPORTED, ULP_EALIGN) are found on the host
+ *    before anything is launched: NOTHING is launched and nothing is written.
+ *    ULP_ELAUNCH reports a HIP launch error.  Every entry point makes a single launch,
+ *    except ulp_k_mean (two) and ulp_group_stats_with_mean (four); when one of their later
+ *    launches fails, the launches queued before it still run, so their workspace and, for
+ *    ulp_group_stats_with_mean, the Q statistics (q_amax, q_minmax) may be written.
  *  - Zero-filling of rows >= used_sequence in Q, K and V is a caller contract
  *    (k_grouped_amax, used_sequence parameter); it is not checked.
  *  - Q and K hold finite values.  The statistics order raw 16-bit patterns, so a NaN in
@@ -79,8 +84,9 @@ enum {
 int64_t ulp_slots(int64_t local_sequence);
 
 /* Consumer scale widths for a live prefix of n rows (unpack_for_sage description: the
- * Sage kernel derives its per-head scale stride from the rows it is given).  Writes
- * ceil(n/64) to both outputs.  Returns ULP_EINVAL when n < 1 or a pointer is NULL. */
+ * consumer's scale tensors are as wide as the number of 64-row groups in the rows handed
+ * to it).  Writes ceil(n/64) to both outputs.  Returns ULP_EINVAL when n < 1 or a pointer
+ * is NULL. */
 int ulp_scale_widths(int64_t n, int64_t* q_width, int64_t* k_width);
 
 /* Bytes of one chunk (source -> destination) for batch B, local_sequence L, local_heads h,
@@ -291,6 +297,8 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
  *   q_amax, k_amax      [P, B, H, slots(L)] float;  q_minmax, k_minmax [P, B, H, 2, 2, D].
  *   k_mean_f32  [B, H, D] float;  k_mean_dtype [B, H, D] dtype (the k_mean_global to pass
  *               on to derive and pack).
+ * Four launches: the Q statistics first, then the K pass, the mean and the K amax.  A
+ * ULP_ELAUNCH from one of the K launches leaves q_amax and q_minmax written.
  * --------------------------------------------------------------------------------- */
 int64_t ulp_group_stats_with_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D,
                                                   int world_size);

@@ -1,8 +1,9 @@
 // ulp_device.h -- device-side building blocks shared by the libulp kernels (gfx950).
 //
-// Arithmetic contract (k_grouped_amax page, description: fp32 convert, subtract, abs,
-// order-independent max, 1e-7 floor): every float operation is a single IEEE binary32
-// operation rounded to nearest-even, fp32 denormals are preserved (the gfx950 default
+// Arithmetic contract (k_grouped_amax page, description): inputs are widened to binary32,
+// centered and taken in magnitude, the group maximum does not depend on the order of the
+// rows, and the result never drops below the 1e-7 floor.  Every float operation is a
+// single IEEE binary32 operation rounded to nearest-even, fp32 denormals are preserved (the gfx950 default
 // float mode), and the library is compiled with -ffp-contract=off so no mul/add pair is
 // fused behind our back.
 #pragma once

@@ -60,6 +60,7 @@ MUTANTS = {
     "v_scale_local_head": ("vf = vf / v_scale[(b * H + hh) * D + d];",
                            "vf = vf / v_scale[(b * H + j) * D + d];"),
     "v_scale_ignored": ("if (v_scale) vf = vf / v_scale[(b * H + hh) * D + d];", ""),
+    "minmax_keeps_negative_zero": ("if (v == 0.0f) v = 0.0f;", ""),
 }
 
 
@@ -73,6 +74,8 @@ def battery(first_failure_only: bool = False):
         ("decode_fp16", lambda: pins.test_input_decoding_matches_library(None, torch.float16)),
         ("worked_example", lambda: pipe.test_hand_worked_example(None)),
         ("padding_only", lambda: pipe.test_padding_only_slice_contributes_floor(None)),
+        ("signed_zero_minmax",
+         lambda: pipe.test_boundary_minmax_signed_zeros(None, torch.bfloat16)),
         ("only_partial_live", lambda: pipe.test_only_partial_live_group_changes(None, 195)),
         ("v_scale_hand", lambda: vsc.test_hand_worked_values(None)),
         ("v_scale_definition", lambda: vsc.test_v_scale_matches_definition(None, vsc.CASES[0])),

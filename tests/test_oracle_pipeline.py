@@ -289,3 +289,53 @@ def test_hand_worked_example(olib):
     q8, k8, v8, qs, ks = res["outs"][1]          # destination 1 owns head 1
     assert ks[0, 0].tolist() == [float(np.float32(f) / np.float32(127))] * 3
     assert (k8[0, :used] == 0).all() and (k8[0, used:] == -127).all()
+
+
+# ------------------------------------------------------------------ signed zeros in min/max
+
+def _bits(x: float) -> int:
+    return int(np.array([x], dtype=np.float32).view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_boundary_minmax_signed_zeros(olib, dtype):
+    """The gathered min/max (derive_k_boundary_amax, gathered_minmax parameter) fixes only a
+    shape; the reading taken is that -0 counts as +0 before the min and max, so each entry
+    has one bit pattern whatever the row order.  B=1, world_size=2, L=96: rank 0's last
+    group is [64,128), its rows 64..95 (the crossing group); rank 1's first group is the
+    same group, rows 96..127.  Every other value is 1.0.  Hand-worked expectations, per
+    channel of head 0 in that group (rank 0 rows 64..95):
+      d0: only -0                    -> min +0, max +0
+      d1: -0 and +0 alternating      -> min +0, max +0
+      d2: -0 with -3.0 and -0.5      -> min -3.0, max +0
+      d3: -0 with +2.0 and +0.25     -> min +0, max +2.0
+      d4: -0 only on rank 1's rows   -> rank 1's first entry: min +0, max +0
+    used_sequence = 100 also makes rank 1's rows >= 100 zero padding (not min/max rows)."""
+    B, P, L, H, D, used = 1, 2, 96, 2, 64, 100
+    S = P * L
+    X = torch.ones(B, S, H, D)
+    X[:, used:] = 0.0
+    rows0 = torch.arange(64, 96)
+    X[0, rows0, 0, 0] = -0.0
+    X[0, rows0, 0, 1] = torch.where(rows0 % 2 == 0, torch.tensor(-0.0), torch.tensor(0.0))
+    X[0, rows0, 0, 2] = -0.0
+    X[0, 70, 0, 2], X[0, 90, 0, 2] = -3.0, -0.5
+    X[0, rows0, 0, 3] = -0.0
+    X[0, 71, 0, 3], X[0, 91, 0, 3] = 2.0, 0.25
+    X[0, 96:used, 0, 4] = -0.0
+    X = X.to(dtype)
+    assert torch.signbit(X[0, 64, 0, 0].float()).item()        # the -0 survives the cast
+    sh = pipeline.shards(X, P)
+    mm0 = oracle.boundary_minmax(sh[0], rank=0, world_size=P, used_sequence=used)
+    mm1 = oracle.boundary_minmax(sh[1], rank=1, world_size=P, used_sequence=used)
+    POS0, NEG3, TWO = _bits(0.0), _bits(-3.0), _bits(2.0)
+    # [b, h, e, s, d]: e = 1 is rank 0's last group, e = 0 is rank 1's first group
+    expect0 = {0: (POS0, POS0), 1: (POS0, POS0), 2: (NEG3, POS0), 3: (POS0, TWO)}
+    for d, (mn, mx) in expect0.items():
+        assert _bits(mm0[0, 0, 1, 0, d].item()) == mn, f"rank 0 min d{d}"
+        assert _bits(mm0[0, 0, 1, 1, d].item()) == mx, f"rank 0 max d{d}"
+    assert _bits(mm1[0, 0, 0, 0, 4].item()) == POS0
+    assert _bits(mm1[0, 0, 0, 1, 4].item()) == POS0
+    # no entry anywhere holds the pattern of -0
+    for mm in (mm0, mm1):
+        assert not (mm.view(torch.int32) == _bits(-0.0) - 2 ** 32).any()
