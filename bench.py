@@ -1,24 +1,27 @@
 """Benchmark of the smooth-K low-precision Ulysses pack/unpack on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input held in HBM:
-fused Q/K statistics (grouped amax + boundary min/max, every rank), the boundary derive,
-the pack of every rank into the all-to-all buffer, and the unpack of every destination --
-four launches on one stream.  Inputs and outputs rotate over several buffer sets so that
-each step reads data last touched several steps earlier (the sets together exceed the
-256 MB last-level cache).
+the Q/K statistics (grouped amax + boundary min/max, every rank), the boundary derive, the
+pack of every rank into the all-to-all buffer, and the unpack of every destination.  Two
+forms of the step give identical bytes: the one-read form (statistics and the pack from
+one read of Q, K and V; then derive with the pack of the slots that waited for it; then
+the unpack: three launches), whose K timed steps give ms_per_step, and the separate form
+(statistics, derive, pack, unpack: four launches, the pages' own sequence), timed the same
+way after it.  The default workload is the largest configuration, long_unaligned (B=1,
+world_size 8, L=9360, H=40, D=128, bf16, used 74000).  Inputs and outputs rotate over
+several buffer sets so that each step reads data last touched several steps earlier (the
+sets together exceed the 256 MB last-level cache).
 
 Timing uses HIP events on the stream every launch goes to, placed only at the two ends of
 each timed region (an event recorded between two launches costs about 2 us of GPU time,
-more than 5 % of a small workload's kernel): the K timed steps give ms_per_step; then K
-launches of each kernel alone give its average duration (pack_ms, unpack_ms, stats_ms,
-derive_ms; the roofline figure uses pack_ms), and K back-to-back pack+unpack pairs give
-the reported value: pack+unpack algorithmic bytes / average pair time.  Each of these
-per-kernel loops is preceded by three untimed calls and timed five times; the median loop
-is reported.  The global K mean
-(an input of the step) is timed the same way, as k_mean GB/s.  The same step with the
-statistics and the pack from one read of Q, K and V (two launches before the unpack instead
-of three; same outputs) is timed likewise and reported as one_read_step_ms.  Prints one
-JSON line.
+more than 5 % of a small workload's kernel).  After the steps, K launches of each kernel
+alone give its average duration (pack_ms, unpack_ms, stats_ms, derive_ms; the roofline
+figure uses pack_ms), and K back-to-back pack+unpack pairs give the reported value:
+pack+unpack algorithmic bytes / average pair time.  Each of these per-kernel loops is
+preceded by three untimed calls and timed five times; the median loop is reported.  The
+global K mean (an input of the step) is timed the same way, as k_mean GB/s.  The CPU
+oracle is timed on the host's cores on the same inputs (cpu_baseline).  Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -109,7 +112,7 @@ def record_traffic(args):
     counters read for a plain device copy of known size, and record the bytes per launch."""
     from precision_attention_input_amd import workloads as W
     fk, wk, fc, wc = args.record_traffic
-    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
+    w = W.BY_NAME[args.workload] if args.workload else W.LONG_UNALIGNED
     copy_bytes = args.copy_calibration * 2 ** 20
     if not copy_bytes:
         raise SystemExit("--record-traffic needs --copy-calibration MIB (the copy's size)")
@@ -133,31 +136,90 @@ def record_traffic(args):
     print(json.dumps(rec))
 
 
-def cpu_baseline(w, d, reps: int):
-    """The CPU oracle's pack+unpack over the whole workload (every rank and destination),
-    repeated `reps` times, single-threaded."""
+def _timed_reps(fn, min_s: float) -> tuple[float, int]:
+    """Mean seconds per call of fn over repetitions totalling at least min_s (at least one)."""
+    n, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return dt / n, n
+
+
+def cpu_baseline(w, d, nb: dict, min_s: float):
+    """The CPU oracle, unchanged, on the host's cores: the ranks' (and destinations')
+    independent calls run side by side on a thread pool (ctypes releases the interpreter
+    lock during each C call), so at most world_size of them run at once.
+      - pack+unpack: the whole workload, every rank's pack then every destination's unpack;
+      - amax: the statistics step, every rank's grouped amax (Q raw, K centered) and
+        boundary min/max of Q and K;
+      - single-thread figures of both on a sample: rank 0's pack + destination 0's unpack,
+        rank 0's statistics (1/world_size of the work).
+    Each figure repeats its work for at least min_s seconds.  GB/s use the GPU figures'
+    algorithmic bytes."""
     import torch
     import oracle
     from oracle import pipeline
 
     P, L = w.P, w.L
+    host_cores = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, host_cores))
+    used_threads = min(threads, P)
     qs, ks, vs = (pipeline.shards(d[n], P) for n in ("Q", "K", "V"))
-    # the amax the pack consumes (computed here, not timed: the metric is pack+unpack)
-    q_amax = [oracle.k_grouped_amax(qs[r], None, rank=r, world_size=P, used_sequence=w.used)
-              for r in range(P)]
-    k_amax = [oracle.k_grouped_amax(ks[r], d["mean"], rank=r, world_size=P,
-                                    used_sequence=w.used) for r in range(P)]
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        sends = [oracle.pack(qs[r], ks[r], vs[r], d["mean"], q_amax[r], k_amax[r], rank=r,
-                             world_size=P) for r in range(P)]
-        for p in range(P):
-            recv = torch.stack([sends[r][p] for r in range(P)])
-            oracle.unpack_for_sage(recv, batch_size=w.B, local_sequence=L, local_heads=w.h,
-                                   head_dim=w.D, world_size=P,
-                                   scale_sequence=w.scale_sequence)
-    dt = (time.perf_counter() - t0) / reps
-    return dt
+    mean = d["mean"]
+    _, _, q_amax, k_amax = pipeline.run_stats(qs, ks, mean, world_size=P,
+                                              used_sequence=w.used, threads=threads)
+
+    def pack_rank(r):
+        return oracle.pack(qs[r], ks[r], vs[r], mean, q_amax[r], k_amax[r], rank=r,
+                           world_size=P)
+
+    def unpack_dest(sends, p):
+        recv = torch.stack([sends[r][p] for r in range(P)])
+        return oracle.unpack_for_sage(recv, batch_size=w.B, local_sequence=L, local_heads=w.h,
+                                      head_dim=w.D, world_size=P,
+                                      scale_sequence=w.scale_sequence)
+
+    def pack_unpack_all():
+        sends = pipeline._map(pack_rank, range(P), threads)
+        pipeline._map(lambda p: unpack_dest(sends, p), range(P), threads)
+
+    sends0 = pipeline._map(pack_rank, range(P), threads)   # destination 0's receive buffer
+
+    def pack_unpack_one():
+        pack_rank(0)
+        unpack_dest(sends0, 0)
+
+    def stats_all():
+        pipeline.run_stats(qs, ks, mean, world_size=P, used_sequence=w.used, threads=threads)
+
+    def stats_one():
+        kw = dict(rank=0, world_size=P, used_sequence=w.used)
+        oracle.boundary_minmax(qs[0], **kw)
+        oracle.boundary_minmax(ks[0], **kw)
+        oracle.k_grouped_amax(qs[0], None, **kw)
+        oracle.k_grouped_amax(ks[0], mean, **kw)
+
+    pu_bytes = nb["pack"] + nb["unpack"]
+    t_pu, n_pu = _timed_reps(pack_unpack_all, min_s)
+    t_st, n_st = _timed_reps(stats_all, min_s / 2)
+    t_pu1, n_pu1 = _timed_reps(pack_unpack_one, min_s / 2)
+    t_st1, n_st1 = _timed_reps(stats_one, min_s / 4)
+    return {
+        "value": round(pu_bytes / t_pu / 1e9, 4), "unit": "GB/s", "cores": used_threads,
+        "kind": "oracle",
+        "sample": f"pack+unpack: the whole workload (pack of all {P} ranks, unpack of all {P} "
+                  f"destinations; {n_pu} repetitions, {t_pu:.3f} s each) with the ranks on "
+                  f"{used_threads} threads of the {host_cores} host cores; single-thread: "
+                  f"rank 0's pack + destination 0's unpack ({n_pu1} repetitions); amax: the "
+                  f"statistics of every rank, Q and K ({n_st} repetitions on {used_threads} "
+                  f"threads; single-thread: rank 0, {n_st1} repetitions)",
+        "single_thread_gbps": round(pu_bytes / P / t_pu1 / 1e9, 4),
+        "amax_gbps": round(nb["stats"] / t_st / 1e9, 4),
+        "amax_single_thread_gbps": round(nb["stats"] / P / t_st1 / 1e9, 4),
+        "host_cores": host_cores,
+    }
 
 
 MFMA_PEAK_TFLOPS = 5000.0       # MI355X dense int8 / fp8 matrix peak
@@ -217,11 +279,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
-                    help="workload name (default: the unaligned padded fp16 workload)")
+                    help="workload name (default: long_unaligned, the largest configuration, "
+                         "B=1, world_size 8, L=9360, H=40, D=128, bf16, used 74000)")
     ap.add_argument("--sets", type=int, default=0, help="rotating buffer sets (0 = auto)")
-    ap.add_argument("--cpu-reps", type=int, default=20,
-                    help="repetitions of the whole workload through the CPU oracle (about 10 s "
-                         "of single-threaded CPU work on the default workload)")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="seconds of repetitions behind the CPU oracle's pack+unpack figure "
+                         "(the amax and single-thread figures take half and a quarter of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--consumer", action="store_true",
                     help="time the MFMA consumer check (INT8 Q.K, FP8 P.V attention over every "
@@ -271,7 +334,7 @@ def main():
                           "dispatches": args.warmup + args.steps}), flush=True)
         return
 
-    w = W.BY_NAME[args.workload] if args.workload else W.UNALIGNED_PADDED
+    w = W.BY_NAME[args.workload] if args.workload else W.LONG_UNALIGNED
     d = W.generate(w)
     if args.consumer:
         consumer_bench(args, w, d, dev)
@@ -359,14 +422,39 @@ def main():
         timed.wall_ms = statistics.median(walls)
         return statistics.median(loops)
 
-    for i in range(max(args.warmup, nsets)):      # every set gets valid statistics
+    # The one-read step: statistics and the pack of every slot that derive cannot change
+    # from one read of Q, K and V, then derive together with the pack of the slots that
+    # waited for it, then the unpack (the same outputs as the separate step above).
+    def stats_pack(s):
+        ulp.group_stats_pack(s["Q"], s["K"], s["V"], s["mean"], world_size=P,
+                             used_sequence=w.used, v_scale=vsc, out=s["stats"],
+                             group=s["group"])
+
+    def derive_pack(s):
+        qa, ka, qm, km = s["stats"]
+        ulp.group_derive_pack(s["Q"], s["K"], s["mean"], qa, ka, qm, km, world_size=P,
+                              group=s["group"], used_sequence=w.used)
+
+    def one_read_step(s):
+        stats_pack(s)
+        derive_pack(s)
+        unpack(s)
+
+    # Warm-up: W steps of each form (at least one per buffer set, so that every set holds
+    # valid statistics for the per-kernel loops below).
+    for i in range(max(args.warmup, nsets)):
         step(sets[i % nsets])
+    for i in range(max(args.warmup, nsets)):
+        one_read_step(sets[i % nsets])
     torch.cuda.synchronize()
 
-    # The timed steps: the whole path, K steps.
+    # The timed steps: the whole path, exactly K steps of the one-read form (ms_per_step,
+    # host clock around them, synchronized on both sides), then K of the separate form.
     K = args.steps
-    step_ms = timed(step, K, warm=0)           # exactly the K steps (warm-up done above)
-    ms_per_step = timed.wall_ms                # host clock around them, synchronized
+    or_step_ms = timed(one_read_step, K, warm=0)
+    ms_per_step = timed.wall_ms
+    step_ms = timed(step, K, warm=0)
+    sep_step_wall_ms = timed.wall_ms
 
     # Each kernel on its own, and pack+unpack as a pair: loops of K launches on the same
     # sets, the median of REPS loops.
@@ -410,27 +498,7 @@ def main():
     sm_sep_ms = timed(stats_mean_separate, K)
     sm_one_ms = timed(stats_mean_one_read, K)
 
-    # The one-read step: statistics and the pack of every slot that derive cannot change
-    # from one read of Q, K and V, then derive together with the pack of the slots that
-    # waited for it, then the unpack (same outputs as the step above).
-    def stats_pack(s):
-        ulp.group_stats_pack(s["Q"], s["K"], s["V"], s["mean"], world_size=P,
-                             used_sequence=w.used, v_scale=vsc, out=s["stats"],
-                             group=s["group"])
-
-    def derive_pack(s):
-        qa, ka, qm, km = s["stats"]
-        ulp.group_derive_pack(s["Q"], s["K"], s["mean"], qa, ka, qm, km, world_size=P,
-                              group=s["group"], used_sequence=w.used)
-
-    def one_read_step(s):
-        stats_pack(s)
-        derive_pack(s)
-        unpack(s)
-
-    for i in range(max(args.warmup, nsets)):
-        one_read_step(sets[i % nsets])
-    or_step_ms = timed(one_read_step, K, REPS)
+    # The one-read step's two pack launches, each alone.
     sp_ms = timed(stats_pack, K, REPS)
     pd_ms = timed(derive_pack, K, REPS)
 
@@ -441,12 +509,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        dt = cpu_baseline(w, d, args.cpu_reps)
-        cpu = {"value": round(pu_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"the whole workload: pack of all {P} ranks + unpack of all {P} "
-                         f"destinations, mean of {args.cpu_reps} repetitions "
-                         f"({dt:.3f} s each), single-threaded C oracle"}
+        cpu = cpu_baseline(w, d, nb, args.cpu_seconds)
 
     line = {
         "metric": "pack+unpack GB/s and % of HBM peak per config; amax-kernel GB/s",
@@ -482,7 +545,9 @@ def main():
                              "stats_pack": round(sp_ms, 5),
                              "derive_pack": round(pd_ms, 5),
                              "stats_pack_gbps": round(nb["pack"] / (sp_ms * 1e-3) / 1e9, 2)},
-        "step_ms_events": round(step_ms, 5),
+        "one_read_step_gbps": round((pu_bytes + nb["stats"] - 2 * 2 * nb["N"]) /
+                                    (or_step_ms * 1e-3) / 1e9, 2),
+        "separate_step_ms": {"events": round(step_ms, 5), "wall": round(sep_step_wall_ms, 5)},
         "step_gbps": round((pu_bytes + nb["stats"]) / (step_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -42,55 +42,62 @@ class UlpError(RuntimeError):
 
 def lib():
     """The loaded libulp.so; raises if it has not been built."""
-    global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is missing: build it first (python -c "
-                "'import __graft_entry__ as g; g.build()')")
-        L = ctypes.CDLL(LIB_PATH)
-        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-        sig = {
-            "ulp_slots": ([i64], i64),
-            "ulp_scale_widths": ([i64, vp, vp], i32),
-            "ulp_chunk_bytes": ([i64, i64, i64, i64], i64),
-            "ulp_last_error": ([], ctypes.c_char_p),
-            "ulp_k_grouped_amax": ([vp, vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
-            "ulp_boundary_minmax": ([vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
-            "ulp_derive_k_boundary_amax": ([vp, vp, vp, i32, i64, i64, i64, i32, i64, i32, vp],
-                                           i32),
-            "ulp_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64,
-                          vp], i32),
-            "ulp_unpack_for_sage": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp,
-                                     vp], i32),
-            "ulp_group_stats": ([vp, vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, vp, vp, vp,
+        load(LIB_PATH)
+    return _lib
+
+
+def load(path: str = LIB_PATH):
+    """Load the library at ``path`` (a build of the same sources) and route every call of
+    this module to it from now on; returns it.  Raises if the file does not exist."""
+    global _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -c "
+            "'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sig = {
+        "ulp_slots": ([i64], i64),
+        "ulp_scale_widths": ([i64, vp, vp], i32),
+        "ulp_chunk_bytes": ([i64, i64, i64, i64], i64),
+        "ulp_last_error": ([], ctypes.c_char_p),
+        "ulp_k_grouped_amax": ([vp, vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
+        "ulp_boundary_minmax": ([vp, i32, i64, i64, i64, i64, i32, i32, i64, vp, vp], i32),
+        "ulp_derive_k_boundary_amax": ([vp, vp, vp, i32, i64, i64, i64, i32, i64, i32, vp],
+                                       i32),
+        "ulp_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, i64,
+                      vp], i32),
+        "ulp_unpack_for_sage": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp,
                                  vp], i32),
-            "ulp_group_derive": ([vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp], i32),
-            "ulp_group_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, vp,
-                                vp], i32),
-            "ulp_group_unpack": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp],
-                                 i32),
-            "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
-            "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
-            "ulp_group_stats_with_mean_workspace_bytes": ([i64, i64, i64, i64, i32], i64),
-            "ulp_group_stats_with_mean": ([vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, i64,
-                                           vp, vp, vp, vp, vp, vp, vp], i32),
-            "ulp_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i32, i64, vp,
-                                vp, vp, vp, vp, i64, vp], i32),
-            "ulp_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32,
-                                 i64, vp, i64, vp], i32),
-            "ulp_group_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i64, vp,
-                                      vp, vp, vp, vp, vp], i32),
-            "ulp_group_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32,
-                                       i64, vp, vp], i32),
-            "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
-                                        vp, vp], i32),
-        }
-        for name, (args, res) in sig.items():
-            f = getattr(L, name)
-            f.argtypes = args
-            f.restype = res
-        _lib = L
+        "ulp_group_stats": ([vp, vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, vp, vp, vp,
+                             vp], i32),
+        "ulp_group_derive": ([vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i32, vp], i32),
+        "ulp_group_pack": ([vp, vp, vp, vp, i32, vp, vp, vp, i64, i64, i64, i64, i32, vp,
+                            vp], i32),
+        "ulp_group_unpack": ([vp, i64, i64, i64, i64, i32, i32, i64, vp, vp, vp, vp, vp, vp],
+                             i32),
+        "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
+        "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
+        "ulp_group_stats_with_mean_workspace_bytes": ([i64, i64, i64, i64, i32], i64),
+        "ulp_group_stats_with_mean": ([vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, i64,
+                                       vp, vp, vp, vp, vp, vp, vp], i32),
+        "ulp_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i32, i64, vp,
+                            vp, vp, vp, vp, i64, vp], i32),
+        "ulp_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32,
+                             i64, vp, i64, vp], i32),
+        "ulp_group_stats_pack": ([vp, vp, vp, vp, i32, vp, i64, i64, i64, i64, i32, i64, vp,
+                                  vp, vp, vp, vp, vp], i32),
+        "ulp_group_derive_pack": ([vp, vp, vp, i32, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                   i64, vp, vp], i32),
+        "ulp_consumer_attention": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                    vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
     return _lib
 
 

@@ -11,6 +11,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libulp.so")
+# The same sources with every launch taking its streaming (non-temporal) instantiation, at
+# any size: a test build, so that small parity cases exercise the code paths that
+# otherwise only launches above the cache budget take.
+STREAM_LIB = os.path.join(HERE, "libulp_stream.so")
+STREAM_FLAGS = ["-DULP_RESIDENT_MB=0"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -37,19 +42,35 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile libulp.so in-tree (atomically replaced) and return its path."""
+def _start(out: str, extra: list[str] | None, verbose: bool):
     tmp = f"{out}.tmp{os.getpid()}"
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, *sources(),
            "-o", tmp]
     if verbose:
         print(" ".join(cmd))
-    proc = subprocess.run(cmd, capture_output=True, text=True)
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    return proc, tmp, out
+
+
+def _finish(job) -> str:
+    proc, tmp, out = job
+    _, err = proc.communicate()
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-6000:]}")
-    os.replace(tmp, out)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{err[-6000:]}")
+    os.replace(tmp, out)    # atomic: a loader never sees a partial file
     return out
 
 
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile libulp.so in-tree (atomically replaced) and return its path."""
+    return _finish(_start(out, extra, verbose))
+
+
+def build_all(verbose: bool = False) -> list[str]:
+    """libulp.so and the streaming test build libulp_stream.so, compiled side by side."""
+    jobs = [_start(LIB, None, verbose), _start(STREAM_LIB, STREAM_FLAGS, verbose)]
+    return [_finish(j) for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

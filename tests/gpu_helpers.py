@@ -44,6 +44,34 @@ def to_dev(d: dict, P: int) -> dict:
     return out
 
 
+def _poisoned_group(w: W.Workload) -> torch.Tensor:
+    """An all-to-all buffer whose every byte starts as 0x5A, so that a byte the kernels
+    leave unwritten cannot match the oracle by chance (torch.empty may hand back memory
+    that still holds an earlier run's identical bytes)."""
+    cb = ulp.chunk_bytes(w.B, w.L, w.h, w.D)
+    return torch.full((w.P, w.P, cb), 0x5A, dtype=torch.uint8, device=DEV)
+
+
+def _poisoned_stats(lead: tuple, w: W.Workload) -> tuple:
+    f = dict(dtype=torch.float32, device=DEV)
+    sl = ulp.slots(w.L)
+    return (torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f),
+            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f))
+
+
+def _poisoned_unpack(w: W.Workload, lead: tuple = ()) -> tuple:
+    """Unpack outputs (q8, k8, v8, q_scale, k_scale) filled with 0x5A bytes / NaN."""
+    qk, vs, sc = ulp.unpack_shapes(w.B, w.L, w.h, w.D, w.P, w.scale_sequence)
+    i8 = dict(dtype=torch.int8, device=DEV)
+    f = dict(dtype=torch.float32, device=DEV)
+    return (torch.full((*lead, *qk), 0x5A, **i8), torch.full((*lead, *qk), 0x5A, **i8),
+            torch.full((*lead, *vs), 0x5A, dtype=torch.uint8, device=DEV).view(
+                torch.float8_e4m3fn),
+            torch.full((*lead, *sc), float("nan"), **f), torch.full((*lead, *sc), float("nan"), **f))
+
+
 def run_per_rank(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     """Every rank through the per-rank entry points; the all-to-all is the [P,P,cb] buffer.
     v_scale: optional [B,H,D] float32 device tensor (the caller's V divisor)."""
@@ -52,17 +80,23 @@ def run_per_rank(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     qs = [dd["Q"][r] for r in range(P)]
     ks = [dd["K"][r] for r in range(P)]
     vs = [dd["V"][r] for r in range(P)]
-    q_mm = torch.stack([ulp.boundary_minmax(qs[r], rank=r, **kw) for r in range(P)])
-    k_mm = torch.stack([ulp.boundary_minmax(ks[r], rank=r, **kw) for r in range(P)])
-    qa = [ulp.k_grouped_amax(qs[r], None, rank=r, **kw) for r in range(P)]
-    ka = [ulp.k_grouped_amax(ks[r], dd["mean"], rank=r, **kw) for r in range(P)]
+    # per-rank outputs of their own (a rank's slice of a stacked tensor need not be
+    # 16-byte aligned), poisoned
+    po = [_poisoned_stats((), w) for _ in range(P)]
+    q_mm = torch.stack([ulp.boundary_minmax(qs[r], rank=r, out=po[r][2], **kw)
+                        for r in range(P)])
+    k_mm = torch.stack([ulp.boundary_minmax(ks[r], rank=r, out=po[r][3], **kw)
+                        for r in range(P)])
+    qa = [ulp.k_grouped_amax(qs[r], None, rank=r, out=po[r][0], **kw) for r in range(P)]
+    ka = [ulp.k_grouped_amax(ks[r], dd["mean"], rank=r, out=po[r][1], **kw)
+          for r in range(P)]
     qa_kernel = [a.clone() for a in qa]
     ka_kernel = [a.clone() for a in ka]
     for r in range(P):
         ulp.derive_k_boundary_amax(qa[r], q_mm, None, rank=r, local_sequence=L, world_size=P)
         ulp.derive_k_boundary_amax(ka[r], k_mm, dd["mean"], rank=r, local_sequence=L,
                                    world_size=P)
-    grp = ulp.group_buffer(w.B, L, w.H, w.D, P, DEV)
+    grp = _poisoned_group(w)
     cb = grp.shape[-1]
     for r in range(P):
         ulp.pack(qs[r], ks[r], vs[r], dd["mean"], qa[r], ka[r], rank=r, world_size=P,
@@ -71,7 +105,8 @@ def run_per_rank(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     for p in range(P):
         outs[p] = ulp.unpack_for_sage(grp[p], batch_size=w.B, local_sequence=L,
                                       local_heads=w.h, head_dim=w.D, world_size=P,
-                                      aligned=aligned, scale_sequence=w.scale_sequence)
+                                      aligned=aligned, scale_sequence=w.scale_sequence,
+                                      out=_poisoned_unpack(w))
     torch.cuda.synchronize()
     return dict(q_minmax=q_mm, k_minmax=k_mm, q_amax_kernel=qa_kernel, k_amax_kernel=ka_kernel,
                 q_amax=qa, k_amax=ka, group=grp,
@@ -82,13 +117,14 @@ def run_group(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     """The whole group through the group entry points (the benchmark's launch sequence)."""
     P, L = w.P, w.L
     qa, ka, qm, km = ulp.group_stats(dd["Q"], dd["K"], dd["mean"], world_size=P,
-                                     used_sequence=w.used)
+                                     used_sequence=w.used, out=_poisoned_stats((P,), w))
     qa_kernel, ka_kernel = qa.clone(), ka.clone()
     ulp.group_derive(qa, ka, qm, km, dd["mean"], local_sequence=L, world_size=P)
     grp = ulp.group_pack(dd["Q"], dd["K"], dd["V"], dd["mean"], qa, ka, world_size=P,
-                         v_scale=v_scale)
+                         v_scale=v_scale, group=_poisoned_group(w))
     o = ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
-                         world_size=P, aligned=aligned, scale_sequence=w.scale_sequence)
+                         world_size=P, aligned=aligned, scale_sequence=w.scale_sequence,
+                         out=_poisoned_unpack(w, (P,)))
     torch.cuda.synchronize()
     return dict(q_minmax=qm, k_minmax=km, q_amax_kernel=list(qa_kernel),
                 k_amax_kernel=list(ka_kernel), q_amax=list(qa), k_amax=list(ka), group=grp,
@@ -113,42 +149,6 @@ def compare_all(g: dict, ref: dict, w: W.Workload, label: str):
             assert_bits_equal(g["outs"][p][i], ref["outs"][p][i], f"{label} {name} dest {p}")
 
 
-def sub_heads(g: dict, w: W.Workload, heads: list[int]) -> dict:
-    """Restrict a GPU result to the sampled heads (one per destination, in order), in the
-    layout of the oracle's result on the sub-problem with H' = P, h' = 1."""
-    P = w.P
-    idx = torch.tensor(heads)
-    res = dict(
-        q_minmax=g["q_minmax"].cpu()[:, :, idx], k_minmax=g["k_minmax"].cpu()[:, :, idx],
-        q_amax_kernel=[a.cpu()[:, idx] for a in g["q_amax_kernel"]],
-        k_amax_kernel=[a.cpu()[:, idx] for a in g["k_amax_kernel"]],
-        q_amax=[a.cpu()[:, idx] for a in g["q_amax"]],
-        k_amax=[a.cpu()[:, idx] for a in g["k_amax"]], outs={})
-    for p in range(P):
-        j = heads[p] - p * w.h
-        q8, k8, v8, qs, ks = (t.cpu() for t in g["outs"][p])
-        res["outs"][p] = (q8[:, :, j:j + 1], k8[:, :, j:j + 1], v8[:, :, j:j + 1],
-                          qs[:, j:j + 1], ks[:, j:j + 1])
-    return res
-
-
-def _poisoned_group(w: W.Workload) -> torch.Tensor:
-    """An all-to-all buffer whose every byte starts as 0x5A, so that a byte the kernels
-    leave unwritten cannot match the oracle by chance (torch.empty may hand back memory
-    that still holds an earlier run's identical bytes)."""
-    cb = ulp.chunk_bytes(w.B, w.L, w.h, w.D)
-    return torch.full((w.P, w.P, cb), 0x5A, dtype=torch.uint8, device=DEV)
-
-
-def _poisoned_stats(lead: tuple, w: W.Workload) -> tuple:
-    f = dict(dtype=torch.float32, device=DEV)
-    sl = ulp.slots(w.L)
-    return (torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
-            torch.full((*lead, w.B, w.H, sl), float("nan"), **f),
-            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f),
-            torch.full((*lead, w.B, w.H, 2, 2, w.D), float("nan"), **f))
-
-
 def run_group_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> dict:
     """The whole group through the one-read entry points: group_stats_pack,
     group_derive_pack, group_unpack (outputs start poisoned)."""
@@ -160,7 +160,8 @@ def run_group_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -> d
     ulp.group_derive_pack(dd["Q"], dd["K"], dd["mean"], qa, ka, qm, km, world_size=P,
                           group=grp, used_sequence=w.used)
     o = ulp.group_unpack(grp, batch_size=w.B, local_sequence=L, local_heads=w.h, head_dim=w.D,
-                         world_size=P, aligned=aligned, scale_sequence=w.scale_sequence)
+                         world_size=P, aligned=aligned, scale_sequence=w.scale_sequence,
+                         out=_poisoned_unpack(w, (P,)))
     torch.cuda.synchronize()
     return dict(q_minmax=qm, k_minmax=km, q_amax_kernel=list(qa_kernel),
                 k_amax_kernel=list(ka_kernel), q_amax=list(qa), k_amax=list(ka), group=grp,
@@ -193,7 +194,8 @@ def run_per_rank_one_read(w: W.Workload, dd: dict, aligned=None, v_scale=None) -
     for p in range(P):
         outs[p] = ulp.unpack_for_sage(grp[p], batch_size=w.B, local_sequence=L,
                                       local_heads=w.h, head_dim=w.D, world_size=P,
-                                      aligned=aligned, scale_sequence=w.scale_sequence)
+                                      aligned=aligned, scale_sequence=w.scale_sequence,
+                                      out=_poisoned_unpack(w))
     torch.cuda.synchronize()
     return dict(q_minmax=q_mm, k_minmax=k_mm, q_amax_kernel=qa_kernel, k_amax_kernel=ka_kernel,
                 q_amax=qa, k_amax=ka, group=grp,

@@ -92,3 +92,10 @@ def sign_pattern_columns(S, H, D, used, dtype, seed):
         x[:, :, c] = col
     x[used:] = 0.0
     return x.to(dtype).unsqueeze(0).contiguous()
+
+
+def oracle_threads() -> int:
+    """Threads for running the oracle's independent per-rank calls side by side: the cores
+    this process may use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))

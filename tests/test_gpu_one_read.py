@@ -15,7 +15,7 @@ import precision_attention_input_amd as ulp
 from precision_attention_input_amd import workloads as W
 
 from gpu_helpers import (DEV, assert_bits_equal, compare_all, run_group, run_group_one_read,
-                         run_per_rank_one_read, say, sub_heads, to_dev)
+                         run_per_rank_one_read, say, to_dev)
 from helpers import sign_pattern_columns, small
 from test_gpu_parity import EDGE, RANDOM, oracle_run
 from test_gpu_vscale import oracle_run as oracle_run_vs
@@ -33,41 +33,6 @@ def test_workload_one_read_parity(olib, wname, mode):
     dd = to_dev(d, w.P)
     run = run_group_one_read if mode == "group" else run_per_rank_one_read
     compare_all(run(w, dd, w.aligned), oracle_run(w, d), w, f"{wname}/one-read/{mode}")
-
-
-@pytest.mark.parametrize("wname", [W.VIDEO_DIT_ALIGNED.name, W.LONG_UNALIGNED.name])
-def test_large_workload_one_read(olib, wname):
-    """Sampled heads against the oracle, and every byte of the all-to-all buffer and of the
-    statistics against the separate statistics + derive + pack launches."""
-    w = W.BY_NAME[wname]
-    say(f"[one-read] generating {wname}")
-    d = W.generate(w)
-    heads = W.sample_heads(w, per_dest=1)
-    dd = to_dev(d, w.P)
-    f = run_group_one_read(w, dd, aligned=w.aligned)
-    ref = oracle_run(w, d, heads)
-    ref.pop("sends")
-    compare_all(sub_heads(f, w, heads), ref, w, f"{wname}/one-read/sampled")
-    say(f"[one-read] {wname} against the separate launches")
-    g = run_group(w, dd, aligned=w.aligned)
-    for key in ("q_minmax", "k_minmax"):
-        assert_bits_equal(f[key], g[key], key)
-    for r in range(w.P):
-        for key in ("q_amax_kernel", "k_amax_kernel", "q_amax", "k_amax"):
-            assert_bits_equal(f[key][r], g[key][r], f"{key} r{r}")
-    assert_bits_equal(f["group"], g["group"], "all-to-all buffer")
-    del g
-    # the per-rank one-read entry points give the same bytes as the whole-group launches
-    # (at the long workload each rank's own launch is large enough to stream from HBM)
-    say(f"[one-read] {wname} per-rank")
-    pr = run_per_rank_one_read(w, dd, aligned=w.aligned)
-    for r in range(w.P):
-        assert_bits_equal(pr["k_amax"][r], f["k_amax"][r], f"k_amax r{r}")
-        assert_bits_equal(pr["q_amax"][r], f["q_amax"][r], f"q_amax r{r}")
-    assert_bits_equal(pr["k_minmax"], f["k_minmax"], "k_minmax")
-    assert_bits_equal(pr["group"], f["group"], "all-to-all buffer (per rank)")
-    del dd, f, pr
-    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("w", EDGE, ids=[f"{w.name}_u{w.used}" for w in EDGE])

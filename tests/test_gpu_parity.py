@@ -1,10 +1,10 @@
 """Parity of the HIP path with the CPU oracle, bit for bit, through the C ABI (GPU).
 
 Every intermediate (boundary min/max, kernel amax, derived amax, chunk bytes) and every
-output (q8, k8, v8, q_scale, k_scale) is compared byte for byte.  The five workloads run in
-the whole-group launch configuration the benchmark times, and through the per-rank entry
-points; the two large ones are compared on sampled heads (one per destination), which the
-oracle computes one by one on the corresponding sub-problem.
+output (q8, k8, v8, q_scale, k_scale) is compared byte for byte.  The three smaller
+workloads run here in the whole-group launch configuration the benchmark times and through
+the per-rank entry points; the two large ones, every head of them, in
+test_gpu_large_parity.py.
 """
 from __future__ import annotations
 
@@ -18,21 +18,15 @@ import precision_attention_input_amd as ulp
 from precision_attention_input_amd import workloads as W
 
 from gpu_helpers import (DEV, assert_bits_equal, compare_all, run_group, run_per_rank, say,
-                         sub_heads, to_dev)
+                         to_dev)
 from helpers import sign_pattern_columns, small
 
 pytestmark = pytest.mark.gpu
 
 
-def oracle_run(w, d, heads=None):
-    if heads is None:
-        return pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
-                                  used_sequence=w.used, scale_sequence=w.scale_sequence)
-    idx = torch.tensor(heads)
-    sub = {n: d[n][:, :, idx].contiguous() for n in ("Q", "K", "V")}
-    return pipeline.run_group(sub["Q"], sub["K"], sub["V"], d["mean"][:, idx].contiguous(),
-                              world_size=w.P, used_sequence=w.used,
-                              scale_sequence=w.scale_sequence)
+def oracle_run(w, d):
+    return pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], world_size=w.P,
+                              used_sequence=w.used, scale_sequence=w.scale_sequence)
 
 
 # ----------------------------------------------------------------- small and medium workloads
@@ -48,45 +42,6 @@ def test_workload_full_parity(olib, wname, mode):
     g = run_group(w, dd, aligned=w.aligned) if mode == "group" else run_per_rank(w, dd, w.aligned)
     ref = oracle_run(w, d)
     compare_all(g, ref, w, f"{wname}/{mode}")
-
-
-# ----------------------------------------------------------------- large workloads, sampled
-
-_LARGE = {}
-
-
-def large(wname):
-    if wname not in _LARGE:
-        _LARGE.clear()
-        w = W.BY_NAME[wname]
-        say(f"[parity] generating {wname}")
-        d = W.generate(w)
-        _LARGE[wname] = (w, d)
-    return _LARGE[wname]
-
-
-@pytest.mark.parametrize("wname", [W.VIDEO_DIT_ALIGNED.name, W.LONG_UNALIGNED.name])
-def test_large_workload_sampled_heads(olib, wname):
-    w, d = large(wname)
-    heads = W.sample_heads(w, per_dest=1)
-    say(f"[parity] {wname} group launch, sampled heads {heads}")
-    dd = to_dev(d, w.P)
-    g = run_group(w, dd, aligned=w.aligned)
-    ref = oracle_run(w, d, heads)
-    ref.pop("sends")
-    compare_all(sub_heads(g, w, heads), ref, w, f"{wname}/sampled")
-    # the per-rank entry points give the same bytes as the group launch, everywhere
-    say(f"[parity] {wname} per-rank vs group")
-    pr = run_per_rank(w, dd, aligned=w.aligned)
-    for r in range(w.P):
-        assert_bits_equal(pr["k_amax"][r], g["k_amax"][r], f"k_amax r{r}")
-        assert_bits_equal(pr["q_amax"][r], g["q_amax"][r], f"q_amax r{r}")
-    assert_bits_equal(pr["group"], g["group"], "all-to-all buffer")
-    for p in range(w.P):
-        for i in range(5):
-            assert_bits_equal(pr["outs"][p][i], g["outs"][p][i], f"output {i} dest {p}")
-    del dd, g, pr
-    torch.cuda.empty_cache()
 
 
 # ----------------------------------------------------------------- enumeration of edge shapes
