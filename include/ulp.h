@@ -21,7 +21,9 @@
  *  - stream is a hipStream_t passed as void* (NULL = the default stream).  Calls are
  *    asynchronous on that stream and never synchronize the host.
  *  - The library allocates no device memory and keeps no state between calls except a
- *    thread-local error message.  The caller owns every buffer.
+ *    thread-local error message and, for ulp_k_mean_noalloc, its per-GPU scratch array
+ *    (device memory that is part of the library, not allocated).  The caller owns every
+ *    buffer.
  *  - Outputs must not alias inputs (except the amax that the derive calls update in
  *    place: ulp_derive_k_boundary_amax, ulp_group_derive, ulp_derive_pack,
  *    ulp_group_derive_pack).
@@ -31,7 +33,8 @@
  *    Argument errors (ULP_EINVAL, ULP_EUNSUPPORTED, ULP_EALIGN) are found on the host
  *    before anything is launched: NOTHING is launched and nothing is written.
  *    ULP_ELAUNCH reports a HIP launch error.  Every entry point makes a single launch,
- *    except ulp_k_mean (two) and ulp_group_stats_with_mean (four); when one of their later
+ *    except ulp_k_mean and ulp_k_mean_noalloc (two) and ulp_group_stats_with_mean (four);
+ *    when one of their later
  *    launches fails, the launches queued before it still run, so their workspace and, for
  *    ulp_group_stats_with_mean, the Q statistics (q_amax, q_minmax) may be written.
  *  - Zero-filling of rows >= used_sequence in Q, K and V is a caller contract
@@ -281,6 +284,20 @@ int64_t ulp_k_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D, i
 int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
                int world_size, int64_t used_sequence, void* workspace, int64_t workspace_bytes,
                float* mean_f32, void* mean_dtype, void* stream);
+
+/* ulp_k_mean for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * bits, with the workspace taken from a device array inside the library instead of an
+ * argument.  The library holds 16 MiB of it per GPU it runs on until the process ends
+ * (enough for K of up to 2 GiB at any shape); a shape whose ulp_k_mean_workspace_bytes()
+ * exceeds that returns ULP_EINVAL with nothing launched.  Every call on one GPU uses that
+ * GPU's single array, so calls that overlap on one GPU (on two streams, or from two
+ * threads) race; calls in stream order do not.  The array's contents on entry do not
+ * matter.  Allocates nothing and calls no allocating routine; the first call on a device
+ * looks up the array's device address.  Arguments as ulp_k_mean. */
+int ulp_k_mean_noalloc(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+                       int world_size, int64_t used_sequence, float* mean_f32,
+                       void* mean_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * Statistics of every rank together with the global K mean, reading Q and K once each.

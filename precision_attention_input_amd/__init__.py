@@ -22,6 +22,7 @@ __all__ = [
     "ULP_NONE", "GROUP_ROWS", "UlpError", "lib", "slots", "chunk_bytes", "scale_widths",
     "k_grouped_amax", "boundary_minmax", "derive_k_boundary_amax", "pack", "unpack_for_sage",
     "group_stats", "group_derive", "group_pack", "group_unpack", "group_buffer", "k_mean",
+    "k_mean_noalloc",
     "group_stats_with_mean", "consumer_attention", "stats_pack", "derive_pack",
     "group_stats_pack", "group_derive_pack",
     "unpack_shapes",
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH):
                              i32),
         "ulp_k_mean_workspace_bytes": ([i64, i64, i64, i64, i32, i64], i64),
         "ulp_k_mean": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, i64, vp, vp, vp], i32),
+        "ulp_k_mean_noalloc": ([vp, i32, i64, i64, i64, i64, i32, i64, vp, vp, vp], i32),
         "ulp_group_stats_with_mean_workspace_bytes": ([i64, i64, i64, i64, i32], i64),
         "ulp_group_stats_with_mean": ([vp, vp, i32, i64, i64, i64, i64, i32, i64, vp, i64,
                                        vp, vp, vp, vp, vp, vp, vp], i32),
@@ -409,6 +411,18 @@ def k_mean(k, *, world_size, used_sequence=None, workspace=None, out=None):
     _check(lib().ulp_k_mean(_p(k), _dt(k), B, L, H, D, world_size, _none(used_sequence),
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _p(mf), _p(md), _stream(k)))
+    return mf, md
+
+
+def k_mean_noalloc(k, *, world_size, out, used_sequence=None):
+    """``k_mean`` without a workspace argument: the library's own device scratch array
+    serves as workspace (nothing is allocated, here or in the library).  ``out`` = (mean
+    fp32 [B,H,D], mean in the dtype [B,H,D] or None) must be given."""
+    P, B, L, H, D = k.shape
+    mf, md = out
+    _dev(k, mf, md)
+    _check(lib().ulp_k_mean_noalloc(_p(k), _dt(k), B, L, H, D, world_size,
+                                    _none(used_sequence), _p(mf), _p(md), _stream(k)))
     return mf, md
 
 

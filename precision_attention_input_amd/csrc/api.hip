@@ -487,6 +487,25 @@ int ulp_k_mean(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_
     return launched(ulp::launch_kmean(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int ulp_k_mean_noalloc(const void* k, int dtype, int64_t B, int64_t L, int64_t H, int64_t D,
+                       int world_size, int64_t used_sequence, float* mean_f32,
+                       void* mean_dtype, void* stream) {
+    const char* fn = "ulp_k_mean_noalloc";
+    TRY(check_shape(fn, dtype, B, L, H, D, world_size, 0, false));
+    TRY(check_seq(fn, "used_sequence", used_sequence, world_size * L));
+    const int64_t need = ulp_k_mean_workspace_bytes(B, L, H, D, world_size, used_sequence);
+    if (need > ulp::kScratchBytes)
+        return fail(ULP_EINVAL, "%s: this shape needs %lld bytes of scratch, more than the "
+                                "library's %lld (use ulp_k_mean with a workspace)", fn,
+                    (long long)need, (long long)ulp::kScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = ulp::scratch_pointer(&scratch);
+    if (e != hipSuccess)
+        return fail(ULP_ELAUNCH, "%s: device scratch address: %s", fn, hipGetErrorString(e));
+    return ulp_k_mean(k, dtype, B, L, H, D, world_size, used_sequence, scratch,
+                      ulp::kScratchBytes, mean_f32, mean_dtype, stream);
+}
+
 int64_t ulp_group_stats_with_mean_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t D,
                                                   int world_size) {
     if (B < 1 || L < 1 || H < 1 || D < 1 || world_size < 1) return 0;

@@ -97,6 +97,11 @@ struct ConsumerLaunch {
     int64_t B, S, h, D, W, used;
 };
 
+// Bytes of the device scratch array of the entry points that allocate nothing, and its
+// address on the current device (looked up once per device).
+constexpr int64_t kScratchBytes = (int64_t)16 << 20;
+hipError_t scratch_pointer(void** out);
+
 // Rows per partial sum of the K mean, and the number of such chunks (workspace rows).
 int64_t kmean_rows(int64_t B, int64_t H, int64_t D, int64_t used);
 int64_t kmean_chunks(int64_t B, int64_t H, int64_t D, int64_t used);

@@ -243,6 +243,20 @@ def test_k_mean_validation(L):
     assert call(B=70000, wsb=1 << 40) == EINVAL and b"too large" in L.ulp_last_error()
 
 
+def test_k_mean_noalloc_rejects_shapes_beyond_its_scratch(L):
+    """The entry point without a workspace argument takes at most 16 MiB of the library's
+    own scratch; a larger need is an argument error, found before any device call."""
+    # B=1, H=64, D=128, used = 2 * 131072: at most 512 rows per partial sum, so 512 partial
+    # rows of 8 * 64 * 128 bytes = 32 MiB
+    need = L.ulp_k_mean_workspace_bytes(1, 131072, 64, 128, 2, NONE)
+    assert need > 16 * 2 ** 20
+    f = ctypes.c_void_p(A)
+    assert L.ulp_k_mean_noalloc(f, 0, 1, 131072, 64, 128, 2, NONE, f, f, None) == EINVAL
+    assert b"scratch" in L.ulp_last_error()
+    assert L.ulp_k_mean_noalloc(f, 0, 1, 100, 4, 96, 2, NONE, f, f, None) == EUNSUPPORTED
+    assert L.ulp_k_mean_noalloc(f, 0, 1, 100, 4, 64, 2, 201, f, f, None) == EINVAL
+
+
 def test_consumer_validation(L):
     def call(B=1, S=128, h=2, D=64, W=2, used=128, v=None):
         return L.ulp_consumer_attention(A, A, A, A, A, v, B, S, h, D, W, used, A, None)
