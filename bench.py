@@ -82,52 +82,83 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, launch_bytes: int):
+def load_traffic(workload: str):
     """HBM bytes per pack launch measured with rocprofv3 counters, if recorded for the
-    current kernel source; None otherwise."""
+    current kernel source: (copy-scaled FETCH_SIZE + WRITE_SIZE, DRAM request bytes), or
+    (None, None)."""
     path = os.path.join(PROFILES, f"pack_kernel_{workload}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_hash") != kernel_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, None
+    return rec.get("hbm_bytes_per_launch"), rec.get("dram_request_bytes_per_launch")
 
 
-def _pmc_values(path: str, kernel: str, counter: str) -> list[float]:
+def _pmc_means(paths: list[str], kernel: str) -> dict:
+    """Mean value per dispatch of every counter recorded for the kernels whose name contains
+    `kernel`, over rocprofv3 counter_collection.csv files."""
     import csv
-    out = []
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
-                out.append(float(r["Counter_Value"]))
-    if not out:
-        raise SystemExit(f"{path}: no {counter} rows for {kernel}")
-    return out
+    vals: dict = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no counter rows for {kernel} in {paths}")
+    return {c: sum(v) / len(v) for c, v in vals.items()}
+
+
+def _need(table: dict, *names):
+    missing = [n for n in names if n not in table]
+    if missing:
+        raise SystemExit(f"counters missing from the files: {missing}")
 
 
 def record_traffic(args):
-    """Scale the pack kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
-    counters read for a plain device copy of known size, and record the bytes per launch."""
+    """HBM bytes per pack launch from rocprofv3 --pmc counter files: the counter_collection.csv
+    files of runs of this script on the workload (--record-traffic) and of --copy-calibration
+    MIB, a plain device copy of known size (--copy-counters), recorded under profiles/ with
+    the pack kernel's source hash.  Two
+    measures, both per launch:
+      - FETCH_SIZE and WRITE_SIZE (KiB), each scaled by copy bytes / what the same counter
+        reads for the copy.  On gfx950 the read factor is 2: FETCH_SIZE counts 128-byte read
+        requests through TCC_BUBBLE, which reads 0 here, so each such request is taken as a
+        64-byte one (the copy's TCC_EA0_RDREQ_128B equals its bytes / 128);
+      - the L2's requests to memory in 32-byte units, TCC_EA0_RDREQ_DRAM_32B and
+        TCC_EA0_WRREQ_WRITE_DRAM_32B, times 32, with no calibration (they read the copy's
+        bytes exactly).
+    Both count what leaves the L2 for memory, last-level (Infinity Cache) hits included."""
     from precision_attention_input_amd import workloads as W
-    fk, wk, fc, wc = args.record_traffic
     w = W.BY_NAME[args.workload] if args.workload else W.LONG_UNALIGNED
     copy_bytes = args.copy_calibration * 2 ** 20
     if not copy_bytes:
         raise SystemExit("--record-traffic needs --copy-calibration MIB (the copy's size)")
-    copy_fetch = _pmc_values(fc, "copyBuffer", "FETCH_SIZE")
-    copy_write = _pmc_values(wc, "copyBuffer", "WRITE_SIZE")
-    f_scale = copy_bytes / (1024 * sum(copy_fetch) / len(copy_fetch))
-    w_scale = copy_bytes / (1024 * sum(copy_write) / len(copy_write))
-    kf = _pmc_values(fk, "::pack_kernel<", "FETCH_SIZE")
-    kw = _pmc_values(wk, "::pack_kernel<", "WRITE_SIZE")
-    read = 1024 * sum(kf) / len(kf) * f_scale
-    write = 1024 * sum(kw) / len(kw) * w_scale
+    if not args.copy_counters:
+        raise SystemExit("--record-traffic needs --copy-counters (the copy run's files)")
+    copy = _pmc_means(args.copy_counters, "copyBuffer")
+    pack = _pmc_means(args.record_traffic, "::pack_kernel<")
+    for t in (copy, pack):
+        _need(t, "FETCH_SIZE", "WRITE_SIZE", "TCC_EA0_RDREQ_DRAM_32B_sum",
+              "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+    f_scale = copy_bytes / (1024 * copy["FETCH_SIZE"])
+    w_scale = copy_bytes / (1024 * copy["WRITE_SIZE"])
+    read = 1024 * pack["FETCH_SIZE"] * f_scale
+    write = 1024 * pack["WRITE_SIZE"] * w_scale
+    dram_read = 32 * pack["TCC_EA0_RDREQ_DRAM_32B_sum"]
+    dram_write = 32 * pack["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
     rec = {"kernel": "pack_kernel", "workload": w.name, "kernel_hash": kernel_hash(),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "copy_dram_request_bytes": round(32 * (copy["TCC_EA0_RDREQ_DRAM_32B_sum"] +
+                                                  copy["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"])),
+           "copy_bytes": 2 * copy_bytes,
            "hbm_read_bytes_per_launch": round(read), "hbm_write_bytes_per_launch": round(write),
            "hbm_bytes_per_launch": round(read + write),
+           "dram_request_read_bytes_per_launch": round(dram_read),
+           "dram_request_write_bytes_per_launch": round(dram_write),
+           "dram_request_bytes_per_launch": round(dram_read + dram_write),
            "algorithmic_bytes_per_launch": algorithmic_bytes(w)["pack"]}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"pack_kernel_{w.name}_traffic.json")
@@ -297,11 +328,14 @@ def main():
     ap.add_argument("--v-scale", action="store_true",
                     help="pass a caller-held [B,H,D] V scale to the pack (V divided before "
                          "E4M3); the default converts V unscaled")
-    ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
-                    help="kernel FETCH_SIZE csv, kernel WRITE_SIZE csv, copy FETCH_SIZE csv, "
-                         "copy WRITE_SIZE csv (rocprofv3 --pmc counter_collection files of this "
-                         "script's default run and of --copy-calibration): write the pack "
-                         "kernel's scaled HBM bytes per launch under profiles/ and exit")
+    ap.add_argument("--record-traffic", nargs="+", metavar="CSV",
+                    help="rocprofv3 --pmc counter_collection files of runs of this script on the "
+                         "workload, holding FETCH_SIZE, WRITE_SIZE, "
+                         "TCC_EA0_RDREQ_DRAM_32B_sum and TCC_EA0_WRREQ_WRITE_DRAM_32B_sum: write "
+                         "the pack kernel's HBM bytes per launch under profiles/ and exit")
+    ap.add_argument("--copy-counters", nargs="+", metavar="CSV",
+                    help="with --record-traffic: the counter_collection files of the "
+                         "--copy-calibration run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB per step (the reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -505,7 +539,7 @@ def main():
     pu_bytes = nb["pack"] + nb["unpack"]
     value = pu_bytes / (pu_ms * 1e-3) / 1e9
     pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
-    traffic = None if args.v_scale else load_traffic(w.name, nb["pack"])
+    traffic, traffic_req = (None, None) if args.v_scale else load_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -552,7 +586,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "pack_kernel", "achieved": round(pack_gbps, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(pack_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": nb["pack"]},
+                     "traffic": traffic, "traffic_dram_requests": traffic_req,
+                     "algorithmic_bytes_per_launch": nb["pack"]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -67,12 +67,18 @@ def test_kernel_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
 
 def test_recorded_traffic_belongs_to_the_current_pack_source():
     """The committed rocprofv3 traffic records were taken on the pack as it is now (the
-    benchmark reports no traffic otherwise), and show no wasted re-reads."""
+    benchmark reports no traffic otherwise), one per large workload, and show no wasted
+    re-reads by either counter measure."""
     recs = sorted(glob.glob(os.path.join(ROOT, "profiles", "pack_kernel_*_traffic.json")))
-    assert recs
+    assert len(recs) == 4
     for path in recs:
         with open(path) as f:
             rec = json.load(f)
         assert rec["kernel_hash"] == bench.kernel_hash(), os.path.basename(path)
         ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
         assert 0.99 < ratio < 1.01, (os.path.basename(path), ratio)
+        # the uncalibrated measure (DRAM requests in 32-byte units) agrees, and read the
+        # calibration copy's bytes exactly
+        ratio = rec["dram_request_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+        assert 0.99 < ratio < 1.01, (os.path.basename(path), ratio)
+        assert abs(rec["copy_dram_request_bytes"] / rec["copy_bytes"] - 1) < 1e-4
