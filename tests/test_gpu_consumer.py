@@ -49,13 +49,15 @@ def test_consumer_on_gpu_outputs(olib, wname):
 
 # ----------------------------------------------------------------- the MFMA consumer kernel
 
-# Against attention on the original inputs the FP8 consumer carries, besides the input
-# quantization the exact consumer already shows (bounds COS, REL), the rounding of every
-# probability to E4M3: up to 2^-4 of each weight (the per-element bound below), about
-# 0.06 relative in the worst case.  Held to 0.2 + 0.06 + margin and a cosine 0.01 lower;
-# misread layouts or scales give >= 150 % (tests/test_oracle_consumer.py).
-COS_FP8, REL_FP8 = 0.97, 0.3
-
+# Against attention on the original inputs (ref_in) the FP8 consumer is held to a bound
+# derived per (b, head), with no constant of its own: its elements lie within the
+# per-element FP8-probability bound e of the float64 consumer on the same bytes (exact,
+# checked first), so by the triangle inequality
+#     ||got - ref_in|| <= ||exact - ref_in|| + ||e||,
+# i.e. rel_l2(got) <= rel_l2(exact) + ||e|| / ||ref_in|| =: r, and cos(got, ref_in) >=
+# sqrt(1 - r^2) (a vector within r |ref_in| of ref_in, r < 1, makes at most that angle).
+# How far exact itself lies from ref_in is the input quantization, which
+# test_consumer_on_gpu_outputs holds to COS / REL.
 def _check_mfma_consumer(w, d, g, vs, dests, heads_of, nq, label):
     used = w.used or w.S
     qsel = sorted(set(list(range(0, used, max(1, used // nq))) + [used - 1, used // 2]))
@@ -77,13 +79,19 @@ def _check_mfma_consumer(w, d, g, vs, dests, heads_of, nq, label):
                 ratio = ((got - ref).abs() / bound).max().item()
                 assert ratio <= 1.0, f"{label}: dest {p} b {b} head {j}: error/bound {ratio}"
                 worst = max(worst, ratio)
-                c = consumer.compare(got, consumer.reference_attention(
-                    d["Q"], d["K"], d["V"], b=b, head=hh, queries=qsel, used=used))
+                ref_in = consumer.reference_attention(d["Q"], d["K"], d["V"], b=b, head=hh,
+                                                      queries=qsel, used=used)
+                exact = consumer.compare(ref, ref_in)
+                r = exact["rel_l2"] + float(bound.norm() / ref_in.norm())
+                c = consumer.compare(got, ref_in)
+                c["allowed_rel_l2"] = r
+                assert c["rel_l2"] <= r * (1 + 1e-9), (label, p, b, j, c)
+                if r < 1:
+                    assert c["cos"] >= (1 - r * r) ** 0.5 - 1e-9, (label, p, b, j, c)
                 if e2e is None or c["rel_l2"] > e2e["rel_l2"]:
                     e2e = c
         assert torch.isfinite(out).all()
     say(f"[mfma consumer] {label}: worst error/bound {worst:.3f}, vs inputs {e2e}")
-    assert e2e["cos"] >= COS_FP8 and e2e["rel_l2"] <= REL_FP8, e2e
 
 
 @pytest.mark.parametrize("wname", [w.name for w in W.WORKLOADS])
