@@ -68,12 +68,17 @@ def algorithmic_bytes(w, v_scale: bool = False) -> dict:
     return dict(pack=pack, unpack=unpack, stats=stats, k_mean=k_mean, N=N)
 
 
-def kernel_hash() -> str:
-    """Hash of the pack kernel's source with comments and whitespace removed, so that the
-    recorded traffic stays attached to the code it was measured on, not to its comments."""
+UNPACK_SOURCES = ["precision_attention_input_amd/csrc/unpack.hip",
+                  "precision_attention_input_amd/csrc/ulp_device.h"]
+
+
+def kernel_hash(sources=None) -> str:
+    """Hash of a kernel's source (the pack's by default) with comments and whitespace
+    removed, so that the recorded traffic stays attached to the code it was measured on,
+    not to its comments."""
     import re
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -83,17 +88,19 @@ def kernel_hash() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per pack launch measured with rocprofv3 counters, if recorded for the
-    current kernel source: (copy-scaled FETCH_SIZE + WRITE_SIZE, DRAM request bytes), or
-    (None, None)."""
+    """HBM bytes measured with rocprofv3 counters for the current kernel sources:
+    (pack: copy-scaled FETCH_SIZE + WRITE_SIZE, pack: DRAM request bytes, unpack: DRAM
+    request bytes), each per launch, or None where not recorded for the current source."""
     path = os.path.join(PROFILES, f"pack_kernel_{workload}_traffic.json")
     if not os.path.exists(path):
-        return None, None
+        return None, None, None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_hash") != kernel_hash():
-        return None, None
-    return rec.get("hbm_bytes_per_launch"), rec.get("dram_request_bytes_per_launch")
+    pack_ok = rec.get("kernel_hash") == kernel_hash()
+    unpack_ok = rec.get("unpack_kernel_hash") == kernel_hash(UNPACK_SOURCES)
+    return (rec.get("hbm_bytes_per_launch") if pack_ok else None,
+            rec.get("dram_request_bytes_per_launch") if pack_ok else None,
+            rec.get("unpack_dram_request_bytes_per_launch") if unpack_ok else None)
 
 
 def _pmc_means(paths: list[str], kernel: str) -> dict:
@@ -149,6 +156,10 @@ def record_traffic(args):
     write = 1024 * pack["WRITE_SIZE"] * w_scale
     dram_read = 32 * pack["TCC_EA0_RDREQ_DRAM_32B_sum"]
     dram_write = 32 * pack["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"]
+    unpack = _pmc_means(args.record_traffic, "::unpack_kernel<")
+    _need(unpack, "TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+    unpack_req = 32 * (unpack["TCC_EA0_RDREQ_DRAM_32B_sum"] +
+                       unpack["TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"])
     rec = {"kernel": "pack_kernel", "workload": w.name, "kernel_hash": kernel_hash(),
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "copy_dram_request_bytes": round(32 * (copy["TCC_EA0_RDREQ_DRAM_32B_sum"] +
@@ -159,7 +170,10 @@ def record_traffic(args):
            "dram_request_read_bytes_per_launch": round(dram_read),
            "dram_request_write_bytes_per_launch": round(dram_write),
            "dram_request_bytes_per_launch": round(dram_read + dram_write),
-           "algorithmic_bytes_per_launch": algorithmic_bytes(w)["pack"]}
+           "algorithmic_bytes_per_launch": algorithmic_bytes(w)["pack"],
+           "unpack_kernel_hash": kernel_hash(UNPACK_SOURCES),
+           "unpack_dram_request_bytes_per_launch": round(unpack_req),
+           "unpack_algorithmic_bytes_per_launch": algorithmic_bytes(w)["unpack"]}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"pack_kernel_{w.name}_traffic.json")
     with open(path, "w") as f:
@@ -539,7 +553,11 @@ def main():
     pu_bytes = nb["pack"] + nb["unpack"]
     value = pu_bytes / (pu_ms * 1e-3) / 1e9
     pack_gbps = nb["pack"] / (pack_ms * 1e-3) / 1e9
-    traffic, traffic_req = (None, None) if args.v_scale else load_traffic(w.name)
+    traffic, traffic_req, unpack_req = (None, None, None) if args.v_scale else \
+        load_traffic(w.name)
+    # the pair's HBM bytes as the counters read them (pack + unpack, DRAM requests), when
+    # both are recorded for the current sources
+    pair_req = traffic_req + unpack_req if traffic_req and unpack_req else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -564,6 +582,8 @@ def main():
                    "v_scale": bool(args.v_scale), "buffer_sets": nsets,
                    "hip_graph": bool(args.graph)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "pct_hbm_peak_counters": (None if pair_req is None else
+                                  round(100 * pair_req / (pu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)),
         "pack_unpack_bytes": pu_bytes,
         "pack_unpack_ms": round(pu_ms, 5),
         "pack_ms": round(pack_ms, 5),

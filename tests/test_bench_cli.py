@@ -82,3 +82,8 @@ def test_recorded_traffic_belongs_to_the_current_pack_source():
         ratio = rec["dram_request_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
         assert 0.99 < ratio < 1.01, (os.path.basename(path), ratio)
         assert abs(rec["copy_dram_request_bytes"] / rec["copy_bytes"] - 1) < 1e-4
+        # the unpack's bytes, recorded beside the pack's for the counter-based pair figure
+        assert rec["unpack_kernel_hash"] == bench.kernel_hash(bench.UNPACK_SOURCES)
+        ratio = (rec["unpack_dram_request_bytes_per_launch"] /
+                 rec["unpack_algorithmic_bytes_per_launch"])
+        assert 0.99 < ratio < 1.01, (os.path.basename(path), ratio)
