@@ -339,3 +339,27 @@ def test_boundary_minmax_signed_zeros(olib, dtype):
     # no entry anywhere holds the pattern of -0
     for mm in (mm0, mm1):
         assert not (mm.view(torch.int32) == _bits(-0.0) - 2 ** 32).any()
+
+
+def test_threaded_group_run_equals_sequential(olib):
+    """The parity tests run the oracle's independent per-rank and per-destination calls on a
+    thread pool; every intermediate and output must be the same bytes as the one-thread
+    run (the C calls share no state)."""
+    w = small(B=2, P=8, L=100, H=16, D=64, dtype=torch.float16, used=700, scale_sequence=650,
+              seed=31)
+    d = W.generate(w)
+    kw = dict(world_size=w.P, used_sequence=w.used, scale_sequence=w.scale_sequence)
+    one = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], threads=1, **kw)
+    many = pipeline.run_group(d["Q"], d["K"], d["V"], d["mean"], threads=8, **kw)
+    for key in ("q_minmax", "k_minmax"):
+        assert torch.equal(one[key].view(torch.int32), many[key].view(torch.int32)), key
+    for key in ("q_amax_kernel", "k_amax_kernel", "q_amax", "k_amax", "sends"):
+        for a, b in zip(one[key], many[key]):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.uint8 else
+                               a.view(torch.int32), b.view(torch.uint8) if
+                               b.dtype == torch.uint8 else b.view(torch.int32)), key
+    for p in range(w.P):
+        for a, b in zip(one["outs"][p], many["outs"][p]):
+            assert torch.equal(a.view(torch.uint8) if a.element_size() == 1 else
+                               a.view(torch.int32), b.view(torch.uint8) if
+                               b.element_size() == 1 else b.view(torch.int32)), p
