@@ -80,11 +80,18 @@ struct Tile {
     int64_t head;           // global head of the piece (of the piece read, if !valid)
 };
 
+// LDS of a phase-0 workgroup: the per-wave head maxima and the [row lane][channel] min/max
+// table (both Q and K tiles use the same arrays).
+struct Phase0Lds {
+    float red[4][256 / 64];
+    float col[8][256 + 1];
+};
+
 // Stats, scale and codes of one Q (CENTER false) or K (CENTER true) tile.
 template <int DT, int D, bool NT, bool CENTER>
 __device__ __forceinline__ void qk_tile(const StatsPackParams& p, const Tile& T, int64_t rz,
                                         int64_t rank, uint8_t* send, const uint4* x,
-                                        const uint4& m, int cb) {
+                                        const uint4& m, int cb, Phase0Lds& lds) {
     constexpr int CPB = 256, HPB = CPB / D, PPH = D / 8;
     constexpr int HEAD_MASK = (PPH - 1) | 32;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -110,7 +117,7 @@ __device__ __forceinline__ void qk_tile(const StatsPackParams& p, const Tile& T,
         }
     }
     a = wave_max_xor<HEAD_MASK>(a);
-    __shared__ float red[4][HPB];
+    auto& red = lds.red;
     if ((lane & HEAD_MASK) == 0) red[wave][T.hib] = a;
     __syncthreads();
     const float amax = fmaxf(kFloor, fmaxf(fmaxf(red[0][T.hib], red[1][T.hib]),
@@ -143,7 +150,7 @@ __device__ __forceinline__ void qk_tile(const StatsPackParams& p, const Tile& T,
                 }
             }
         }
-        __shared__ float col[8][CPB + 1];
+        auto& col = lds.col;
         const int64_t ch0 = (int64_t)cb * CPB;
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -297,10 +304,11 @@ __global__ __launch_bounds__(kThreads) void stats_pack0_kernel(StatsPackParams p
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    __shared__ Phase0Lds lds;
     if (t == 0) {
-        qk_tile<DT, D, NT, false>(p, T, rz, rank, send, x, m, cb);
+        qk_tile<DT, D, NT, false>(p, T, rz, rank, send, x, m, cb, lds);
     } else if (t == 1) {
-        qk_tile<DT, D, NT, true>(p, T, rz, rank, send, x, m, cb);
+        qk_tile<DT, D, NT, true>(p, T, rz, rank, send, x, m, cb, lds);
     } else {
         // V needs no statistic: E4M3 of every row of the rank in the group, two rows of 8
         // channels per conversion.
