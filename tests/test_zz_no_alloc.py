@@ -4,7 +4,8 @@ ulp_k_mean with a caller workspace (GPU).
 The no-allocation entry point runs the same kernels over the library's own device scratch
 array, so its means must equal ulp_k_mean's bit for bit.  Calls follow one another on the
 same GPU, each smaller than the one before it or reusing what an earlier call left in the
-shared array, and every output starts poisoned.
+shared array, and every output starts poisoned.  Last, the use it exists for: the call
+captured into a HIP graph and replayed on new inputs.
 """
 from __future__ import annotations
 
@@ -61,3 +62,31 @@ def test_edge_shapes(olib):
         dtype = (torch.bfloat16, torch.float16)[i % 2]
         _both(small(B=1 + i % 2, P=P, L=L, H=H, D=D, dtype=dtype, used=used, seed=40 + i),
               f"edge P={P} L={L} H={H} D={D} used={used}")
+
+
+def test_k_mean_noalloc_in_a_graph(olib):
+    w = small(B=2, P=4, L=300, H=8, D=128, dtype=torch.bfloat16, used=1100, seed=61)
+    P, B, L, H, D = w.P, w.B, w.L, w.H, w.D
+    inputs = []
+    for seed in (61, 62, 63):
+        d = W.generate(w.with_(seed=seed))
+        inputs.append(W.stacked_shards(d["K"], P).to(DEV))
+    K = torch.empty_like(inputs[0])
+    out = (torch.empty(B, H, D, dtype=torch.float32, device=DEV),
+           torch.empty(B, H, D, dtype=w.dtype, device=DEV))
+    K.copy_(inputs[0])
+    ulp.k_mean_noalloc(K, world_size=P, used_sequence=w.used, out=out)   # first call: lookup
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ulp.k_mean_noalloc(K, world_size=P, used_sequence=w.used, out=out)
+    for i, src in enumerate(inputs * 2):
+        K.copy_(src)
+        out[0].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        want = ulp.k_mean(src, world_size=P, used_sequence=w.used)    # eager, own workspace
+        torch.cuda.synchronize()
+        assert_bits_equal(out[0], want[0], f"replay {i}: binary32 mean")
+        assert_bits_equal(out[1], want[1], f"replay {i}: dtype mean")
+        say(f"[no-alloc graph] replay {i}: bit-exact")
