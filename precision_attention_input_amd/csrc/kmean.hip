@@ -29,7 +29,7 @@ namespace {
 constexpr int kWaves = kThreads / 64;
 constexpr int kColsPerBlock = 64 * 8;     // one wave-wide row segment
 constexpr int kMinRows = 32, kMaxRows = 512;
-constexpr int64_t kTargetBlocks = 2048;
+constexpr int64_t kTargetBlocks = 512;
 
 struct KMeanParams {
     const uint16_t* k;
