@@ -341,7 +341,9 @@ int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B
  *              16-byte aligned).
  *   v_scale    [B, h, D] float (this destination's heads) or NULL.
  *   out        [B, used, h, D] float.
- * D is 64 or 128; 1 <= used <= S. */
+ * D is 64 or 128; 1 <= used <= S; one batch entry of k8 (S*h*D bytes) and of v8
+ * (D*h*Spad bytes) must each be below 2 GiB (the kernel addresses a batch entry with 32-bit
+ * offsets), else ULP_EINVAL. */
 int ulp_consumer_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8,
                            const float* q_scale, const float* k_scale, const float* v_scale,
                            int64_t B, int64_t S, int64_t h, int64_t D, int64_t W,

@@ -584,6 +584,9 @@ int ulp_consumer_attention(const int8_t* q8, const int8_t* k8, const uint8_t* v8
                     (long long)W, (long long)width_of(used));
     if (B > 65535 || h > 65535 || B * S > ((int64_t)1 << 40) / (h * D))
         return fail(ULP_EINVAL, "%s: problem too large", fn);
+    const int64_t spad = width_of(S) * ULP_GROUP_ROWS;
+    if (S * h * D >= ((int64_t)1 << 31) || D * h * spad >= ((int64_t)1 << 31))
+        return fail(ULP_EINVAL, "%s: one batch entry of k8 or v8 is 2 GiB or more", fn);
     TRY(check_ptr(fn, "q8", q8));
     TRY(check_ptr(fn, "k8", k8));
     TRY(check_ptr(fn, "v8", v8));

@@ -9,8 +9,9 @@
 //   out[i, d]   = sum_t softmax_t(score(i, .)) * e4m3(v8[d, t]) * v_scale[d]
 // with the INT8 dot products on gfx950's v_mfma_i32_16x16x64_i8 (exact int32) and the P.V
 // product on v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit block scales), P
-// quantized to E4M3 after scaling by 448 (the largest E4M3 value), as an FP8 consumer does.  Smooth K needs no correction: removing a per-channel
-// mean from every key shifts all scores of a query by the same amount.
+// quantized to E4M3 after scaling by 448 (the largest E4M3 value), as an FP8 consumer does.
+// Smooth K needs no correction: removing a per-channel mean from every key shifts all scores
+// of a query by the same amount.
 //
 // Work decomposition: a 256-thread workgroup owns 64 query rows of one (b, head) -- one Q
 // scale group -- and each wave 16 of them.  Key tiles of 128 rows (two K scale groups) and
@@ -34,6 +35,7 @@
 // applied once, when a K row is stored in LDS (slot 16 kb + 4 q + r for key 32 q + 4 kb + r),
 // so every fragment read covers 16 consecutive padded rows.
 #include <cmath>
+#include <type_traits>
 
 #include "ulp_device.h"
 #include "ulp_kernels.h"
@@ -46,10 +48,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kConsumerKeys = 128;   // keys per LDS tile: one P.V MFMA per channel block
-// Waves (16 queries each) per workgroup: they share every K / V tile in LDS, so more waves
-// mean fewer tile loads per query; 8 measured best at D = 128, 4 at D = 64.
-template <int D>
-constexpr int consumer_waves() { return D == 128 ? 8 : 4; }
+// Workgroup shape: WAVES waves of QB 16-query column blocks each.  The QB blocks of a wave
+// share every K / V fragment read from LDS (one fragment feeds QB MFMAs), so LDS traffic
+// per FLOP falls as 1 / QB; the waves of a workgroup share every tile loaded into LDS.
+// The launcher picks the shape (see launch_consumer).
 constexpr int kUnitScale = 127;      // E8M0 block scale 2^0
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
 
@@ -85,212 +87,322 @@ __device__ __forceinline__ float quad_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// LDS tiles: KT keys x D channels of k8 and D channels x KT keys of v8, rows padded by 16
-// bytes (keeps 16-byte writes aligned and spreads the fragment reads over the banks).
+// LDS tiles: KT key slots x D channels of k8 and D channels x KT keys of v8, unpadded.  The
+// 16-byte pieces of each row are stored XOR-permuted by the row index (the piece swizzle
+// below), so the 16 rows x 16 bytes of a fragment read fall in distinct banks.
 template <int D, int KT>
 struct ConsumerTiles {
-    static constexpr int KROW = D + 16, VROW = KT + 16;
-    static constexpr int KBYTES = KT * KROW, VBYTES = D * VROW;
+    static constexpr int KBYTES = KT * D, VBYTES = D * KT;
     uint8_t k[2][KBYTES];
     uint8_t v[2][VBYTES];
 };
 
+// Stored position of 16-byte piece `lp` of K slot `slot` (rows of D bytes: two slots share
+// a 128-byte line at D = 64) and of V row `row` (rows of 128 bytes).  Each is its own
+// inverse, so the same function maps a stored position back to the piece.
 template <int D>
-__global__ __launch_bounds__(64 * consumer_waves<D>()) __attribute__((amdgpu_waves_per_eu(2)))
-void consumer_kernel(
-    ConsumerParams p) {
+__device__ __forceinline__ int k_piece(int slot, int lp) {
+    return D == 128 ? lp ^ (slot & 7) : lp ^ ((slot >> 1) & 3);
+}
+__device__ __forceinline__ int v_piece(int row, int lp) { return lp ^ (row & 7); }
+
+// Buffer resource for raw buffer loads: 64-bit base, stride 0, `bytes` in range (loads at
+// or past it return zeros), default data format.
+__device__ __forceinline__ v4i buffer_resource(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return v4i{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)bytes, 0x00020000};
+}
+
+// Global -> LDS buffer load of 16 bytes per lane: lane l's bytes land at LDS address
+// lds + 16 l (`lds` is the wave's, in M0; the hardware adds the lane offset).  Written as
+// asm so that the compiler, which cannot tell the two LDS tile buffers apart, does not wait
+// for these loads before every later LDS read: the loads into one buffer overlap the reads
+// of the other, and lds_load_barrier() waits for them explicitly.  The asm writes no
+// register the compiler sees (the data goes to LDS); M0 is used by nothing else here.
+__device__ __forceinline__ void buffer_load_lds16(v4i rsrc, uint32_t lds, int voffset) {
+    // rsrc and lds are uniform; readfirstlane makes the compiler hold them in SGPRs
+    const v4i rs = {__builtin_amdgcn_readfirstlane(rsrc[0]),
+                    __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]),
+                    __builtin_amdgcn_readfirstlane(rsrc[3])};
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voffset), "s"(rs) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Wait for all of this wave's outstanding memory operations (the LDS loads included), then
+// for every wave of the workgroup.  The wait is the compiler's own instruction, so it knows
+// that every earlier load has completed and adds no waits of its own after it (a compiler
+// wait would count the LDS loads it does not see and drain them).
+__device__ __forceinline__ void lds_load_barrier() {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+}
+
+template <int D, int QB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void consumer_kernel(ConsumerParams p) {
     constexpr int KT = kConsumerKeys;          // keys per tile
     constexpr int KB = KT / 16;                // 16-key blocks of S^T per tile
     constexpr int KC = D / 64;                 // 64-channel slices of a Q / K row
     constexpr int CB = D / 16;                 // 16-channel blocks of the output
     using T = ConsumerTiles<D, KT>;
-    // global -> LDS copy of one tile: 16 bytes per thread per step
-    constexpr int KV = D / 16;                 // 16-byte pieces of a K row
-    constexpr int VV = KT / 16;                // 16-byte pieces of a V row
-    constexpr int NT = 64 * consumer_waves<D>();   // threads per workgroup
-    constexpr int NQ = 16 * consumer_waves<D>();   // queries per workgroup
-    constexpr int KSTEPS = KT * KV / NT;
-    constexpr int VSTEPS = D * VV / NT;
-    static_assert(KSTEPS * NT == KT * KV && VSTEPS * NT == D * VV, "tile split");
+    constexpr int NQW = 16 * QB;               // queries per wave
+    constexpr int NQ = NQW * WAVES;            // queries per workgroup
+    static_assert(64 % NQW == 0, "a wave's queries share one Q scale group");
+    // global -> LDS copy of one tile pair in 1 KB pieces, one wave instruction each
+    constexpr int NKC = KT * D / 1024, NVC = D * KT / 1024;
+    constexpr int CPW = (NKC + NVC) / WAVES;   // pieces per wave
+    static_assert(CPW * WAVES == NKC + NVC, "tile split");
     __shared__ __align__(16) T tl;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS load bases
     const int col = lane & 15, grp = lane >> 4;
     const int64_t tile = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int64_t hD = p.h * D;
-    const int64_t qi = tile * NQ + wave * 16 + col;   // this lane's query
+    const int64_t qw = tile * NQ + wave * NQW;   // first query of this wave
+    // this lane's query in column block qb: qw + 16 qb + col
 
-    // Q^T fragments (B operand): channels 64c + 16 grp + [0, 16) of query qi.
-    v4i qf[KC];
-    const int8_t* qrow = p.q8 + (b * p.S + qi) * hD + j * D + 16 * grp;
+    // Q^T fragments (B operand): channels 64c + 16 grp + [0, 16) of each of the lane's queries.
+    v4i qf[QB][KC];
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-        qf[c] = qi < p.S ? *reinterpret_cast<const v4i*>(qrow + 64 * c) : v4i{0, 0, 0, 0};
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qi = qw + 16 * qb + col;
+        const int8_t* qrow = p.q8 + (b * p.S + qi) * hD + j * D + 16 * grp;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            qf[qb][c] = qi < p.S ? *reinterpret_cast<const v4i*>(qrow + 64 * c)
+                                 : v4i{0, 0, 0, 0};
+    }
     // Q scale group of this wave's queries; a wave wholly past `used` (it still takes part
     // in the shared tile loads and barriers, its outputs are not stored) reads the last one.
-    const int64_t qg = min((tile * NQ + wave * 16) / 64, p.W - 1);
+    const int64_t qg = min(qw / 64, p.W - 1);
     const float qs = p.q_scale[(b * p.h + j) * p.W + qg] * p.score_scale;
     const float* ksc = p.k_scale + (b * p.h + j) * p.W;
 
-    v4f o[CB];
+    v4f o[QB][CB];
+    float m[QB], lsum[QB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) o[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    float m = -__builtin_inff(), lsum = 0.0f;
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) o[qb][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        m[qb] = -__builtin_inff();
+        lsum[qb] = 0.0f;
+    }
 
     const int64_t ntiles = (p.used + KT - 1) / KT;
     const int8_t* kg = p.k8 + b * p.S * hD + j * D;
     const uint8_t* vg = p.v8 + ((b * D) * p.h + j) * p.spad;
     const int64_t vrow = p.h * p.spad;         // bytes between channel rows of v8
 
-    // Coalesced tile loads into registers (rows of k8 are 16-byte pieces of D bytes; rows
-    // of the tile's v8 are KT bytes of one channel).  K rows past `used` and V columns past
-    // Spad are zero.
-    uint4 kr[KSTEPS], vr[VSTEPS];
-    auto fetch = [&](int64_t t0) {
+    // Tile loads straight into LDS.  Piece c of the pair is K (c < NKC) or V; lane l of
+    // its instruction fills stored bytes 1024 c' + 16 l, i.e. a (row, stored piece), and
+    // loads the global bytes of the logical piece stored there.  K rows past `used` lie at
+    // or past the K range and read as zeros; V columns past Spad are pointed past the V
+    // range (0x80000000) and read as zeros; the ranges end inside batch entry b.
+    const uint32_t vbytes_b = (uint32_t)(D * vrow - j * p.spad);   // vg .. end of entry b
+    auto issue = [&](uint8_t* kd, uint8_t* vd, int64_t t0) {
+        const v4i krs = buffer_resource(kg + t0 * hD, (uint32_t)((p.used - t0) * hD));
+        const v4i vrs = buffer_resource(vg + t0, vbytes_b - (uint32_t)t0);
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const int e = s * NT + tid, row = e / KV, piece = e % KV;
-            const int64_t t = t0 + row;
-            kr[s] = t < p.used ? *reinterpret_cast<const uint4*>(kg + t * hD + 16 * piece)
-                               : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * NT + tid, d = e / VV, piece = e % VV;
-            const int64_t t = t0 + 16 * piece;
-            vr[s] = t < p.spad ? *reinterpret_cast<const uint4*>(vg + d * vrow + t)
-                               : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const int e = s * NT + tid, row = e / KV, piece = e % KV;
-            const int slot = 16 * ((row & 31) >> 2) + 4 * (row >> 5) + (row & 3);
-            *reinterpret_cast<uint4*>(&tl.k[buf][slot * T::KROW + 16 * piece]) = kr[s];
-        }
-#pragma unroll
-        for (int s = 0; s < VSTEPS; ++s) {
-            const int e = s * NT + tid, d = e / VV, piece = e % VV;
-            *reinterpret_cast<uint4*>(&tl.v[buf][d * T::VROW + 16 * piece]) = vr[s];
+        for (int i = 0; i < CPW; ++i) {
+            const int c = wave + WAVES * i;
+            if (c < NKC) {
+                const int off = c * 1024 + 16 * lane;
+                const int slot = off / D, lp = k_piece<D>(slot, (off % D) / 16);
+                // LDS slot 16 kb + 4 q + r holds key 32 q + 4 kb + r of the tile
+                const int key = 32 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
+                buffer_load_lds16(krs, lds_address(kd + c * 1024), key * (int)hD + 16 * lp);
+            } else {
+                const int off = (c - NKC) * 1024 + 16 * lane;
+                const int row = off / KT, lp = v_piece(row, (off % KT) / 16);
+                const int vo = t0 + 16 * lp < p.spad ? row * (int)vrow + 16 * lp
+                                                     : (int)0x80000000;
+                buffer_load_lds16(vrs, lds_address(vd + (c - NKC) * 1024), vo);
+            }
         }
     };
-    fetch(0);
-    stash(0);
-    __syncthreads();
+    // K scale of the lane's 64-key group in the tile starting at t0 (positive; a group past
+    // the scale width holds no live key and takes 1), loaded a tile ahead so that it is in
+    // a register when the tile's barrier has passed.
+    auto k_scale_of = [&](int64_t t0) {
+        const int64_t gi = t0 / 64 + (grp >> 1);
+        return gi < p.W ? ksc[gi] : 1.0f;
+    };
+    float ks_next = k_scale_of(0);
+    issue(tl.k[0], tl.v[0], 0);
+    lds_load_barrier();
 
-    for (int64_t kt = 0; kt < ntiles; ++kt) {
-        const int buf = (int)(kt & 1);
-        const int64_t t0 = kt * KT;
-        if (kt + 1 < ntiles) fetch(t0 + KT);   // in flight while this tile is computed
-        const uint8_t* kl = tl.k[buf];
-        const uint8_t* vl = tl.v[buf];
+    // One tile: start the loads of the next pair (if `next`) into kd / vd, then compute from
+    // kl / vl; the loads complete by the barrier after the step.
+    // `last` (a compile-time tag) marks the final tile, the only one that can hold keys past
+    // `used`; the other tiles carry no masking code.
+    auto step = [&](auto last, const uint8_t* kl, const uint8_t* vl, uint8_t* kd, uint8_t* vd,
+                    int64_t t0, bool next) {
+        const float ks = ks_next;
+        if (next) {
+            ks_next = k_scale_of(t0 + KT);
+            issue(kd, vd, t0 + KT);
+        }
         // S^T, 16 keys per MFMA: row i of block kb is key 32 (i / 4) + 4 kb + i % 4 of the
         // tile, so the accumulator rows 4 grp + r of every block hold this lane's 32
         // consecutive keys 32 grp + 4 kb + r.
-        // (The stash stores key row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block
-        // kb reads 16 consecutive slots: no bank conflicts.)
-        v4i s[KB];
+        // (The loads store key row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block
+        // kb reads 16 consecutive slots.)
+        // Each K fragment read from LDS feeds the MFMAs of all QB column blocks.
+        v4i s[QB][KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            s[kb] = v4i{0, 0, 0, 0};
-            const uint8_t* krow = kl + (16 * kb + col) * T::KROW + 16 * grp;
 #pragma unroll
-            for (int c = 0; c < KC; ++c)
-                s[kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                    *reinterpret_cast<const v4i*>(krow + 64 * c), qf[c], s[kb], 0, 0, 0);
+            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = v4i{0, 0, 0, 0};
+            const int slot = 16 * kb + col;
+            const uint8_t* krow = kl + slot * D;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const v4i kf = *reinterpret_cast<const v4i*>(
+                    krow + 16 * k_piece<D>(slot, grp + 4 * c));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    s[qb][kb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kf, qf[qb][c], s[qb][kb],
+                                                                       0, 0, 0);
+            }
         }
-        // The lane's keys lie in one 64-key K scale group (positive; a group past the scale
-        // width holds no live key and takes 1), so its largest score is its largest dot
-        // product times that scale.  The int32 dot products convert exactly; only the last
-        // tile can hold keys past `used`, which become -inf (no maximum, probability 0).
-        const int live = (int)min((int64_t)KT, p.used - t0);   // live keys of this tile
-        const int64_t gi = t0 / 64 + (grp >> 1);
-        const float scl = gi < p.W ? qs * ksc[gi] : 1.0f;
-        float xf[KB][4];
+        // The lane's keys lie in one 64-key K scale group, so its largest score is its
+        // largest dot product times that scale.  The int32 dot products convert exactly;
+        // only the last tile can hold keys past `used`, which become -inf (no maximum,
+        // probability 0).
+        // key 32 grp + i of the tile is live iff i < lim (compared against the constant i)
+        const int lim = (int)min((int64_t)KT, p.used - t0) - 32 * grp;
+        const float scl = t0 / 64 + (grp >> 1) < p.W ? qs * ks : 1.0f;
+        uint32_t pw[QB][KB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xf[kb][r] = (float)s[kb][r];
-        if (live < KT) {
+        for (int qb = 0; qb < QB; ++qb) {
+            float xf[KB][4];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (32 * grp + 4 * kb + r >= live) xf[kb][r] = -__builtin_inff();
-        }
-        float gmax = -__builtin_inff();
+                for (int r = 0; r < 4; ++r) xf[kb][r] = (float)s[qb][kb][r];
+            if constexpr (decltype(last)::value) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
-        float tmax = gmax * scl;
-        tmax = quad_max(tmax);
-        const float mnew = fmaxf(m, tmax);           // finite: key t0 < used is live
-        // 448 p = exp2(score - mnew + log2(448)), one fma and one exp2 per key; the row sum
-        // is kept in the same 448-scaled units.  The values stay at or below 448 (up to the
-        // exp2 error), so the E4M3 conversion needs no clamp.
-        const float moff = mnew - kLog2_448;
-        float psum = 0.0f;
-        uint32_t pw[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            float pr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], scl, -moff));
-                psum += pr[r];
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * kb + r >= lim) xf[kb][r] = -__builtin_inff();
             }
-            int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
-            w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
-            pw[kb] = (uint32_t)w;
-        }
-        psum = quad_sum(psum);
-        // Rescale the running sums only when some query's maximum moved in this wave.
-        if (__builtin_amdgcn_ballot_w64(mnew != m) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            lsum *= alpha;
+            float gmax = -__builtin_inff();
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) o[cb] *= alpha;
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
+            float tmax = gmax * scl;
+            tmax = quad_max(tmax);
+            const float mnew = fmaxf(m[qb], tmax);   // finite: key t0 < used is live
+            // 448 p = exp2(score - mnew + log2(448)), one fma and one exp2 per key; the row
+            // sum is kept in the same 448-scaled units.  The values stay at or below 448 (up
+            // to the exp2 error), so the E4M3 conversion needs no clamp.
+            const float moff = mnew - kLog2_448;
+            float psum = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], scl, -moff));
+                    psum += pr[r];
+                }
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
+                pw[qb][kb] = (uint32_t)w;
+            }
+            psum = quad_sum(psum);
+            // Rescale the running sums only when some query's maximum moved in this wave.
+            if (__builtin_amdgcn_ballot_w64(mnew != m[qb]) != 0) {
+                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+                lsum[qb] *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) o[qb][cb] *= alpha;
+            }
+            lsum[qb] += psum;
+            m[qb] = mnew;
         }
-        lsum += psum;
-        m = mnew;
         // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 32 grp + 4 kb + r, i.e. in
         // key order; the V^T rows (channels) supply the same 32 consecutive keys.
-        const v8i pf = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
-                        (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        // Each V fragment read from LDS feeds the MFMAs of all QB column blocks.
+        v8i pf[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            pf[qb] = v8i{(int)pw[qb][0], (int)pw[qb][1], (int)pw[qb][2], (int)pw[qb][3],
+                         (int)pw[qb][4], (int)pw[qb][5], (int)pw[qb][6], (int)pw[qb][7]};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-            const uint4* v16 =
-                reinterpret_cast<const uint4*>(vl + (16 * cb + col) * T::VROW + 32 * grp);
-            const uint4 va0 = v16[0], va1 = v16[1];
+            const int row = 16 * cb + col;
+            const uint8_t* vr = vl + row * KT;
+            const uint4 va0 = *reinterpret_cast<const uint4*>(vr + 16 * v_piece(row, 2 * grp));
+            const uint4 va1 =
+                *reinterpret_cast<const uint4*>(vr + 16 * v_piece(row, 2 * grp + 1));
             const v8i va = {(int)va0.x, (int)va0.y, (int)va0.z, (int)va0.w,
                             (int)va1.x, (int)va1.y, (int)va1.z, (int)va1.w};
-            o[cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                va, pf, o[cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                o[qb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    va, pf[qb], o[qb][cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
-        if (kt + 1 < ntiles) stash(buf ^ 1);   // the other buffer: nobody reads it now
-        __syncthreads();
+    };
+    for (int64_t kt = 0; kt + 1 < ntiles; ++kt) {
+        const int buf = (int)(kt & 1);
+        step(std::false_type{}, tl.k[buf], tl.v[buf], tl.k[buf ^ 1], tl.v[buf ^ 1], kt * KT,
+             true);
+        lds_load_barrier();   // the next pair has landed; this one is no longer read
+    }
+    {
+        const int buf = (int)((ntiles - 1) & 1);
+        step(std::true_type{}, tl.k[buf], tl.v[buf], tl.k[buf ^ 1], tl.v[buf ^ 1],
+             (ntiles - 1) * KT, false);
+    }
+    // The last tile's results are used only by the lanes of live queries (the branch
+    // below).  MFMAs need every lane of the wave, so they must not run inside that branch:
+    // an opaque use of every accumulator here, where all lanes are active, keeps the
+    // compiler from moving the last tile's MFMAs (or anything feeding them) into it.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(o[qb][cb]));
+        asm volatile("" : "+v"(lsum[qb]));
     }
 
-    if (qi >= p.used) return;
-    const float inv = 1.0f / lsum;                 // lsum is in 448-scaled units
-    float* orow = p.out + (b * p.used + qi) * hD + j * D;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int d0 = cb * 16 + 4 * grp;
-        float4 r = make_float4(o[cb][0] * inv, o[cb][1] * inv, o[cb][2] * inv, o[cb][3] * inv);
-        if (p.v_scale) {
-            const float4 vs =
-                *reinterpret_cast<const float4*>(p.v_scale + (b * p.h + j) * D + d0);
-            r.x *= vs.x;
-            r.y *= vs.y;
-            r.z *= vs.z;
-            r.w *= vs.w;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t qi = qw + 16 * qb + col;
+        if (qi >= p.used) continue;
+        const float inv = 1.0f / lsum[qb];         // lsum is in 448-scaled units
+        float* orow = p.out + (b * p.used + qi) * hD + j * D;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int d0 = cb * 16 + 4 * grp;
+            float4 r = make_float4(o[qb][cb][0] * inv, o[qb][cb][1] * inv,
+                                   o[qb][cb][2] * inv, o[qb][cb][3] * inv);
+            if (p.v_scale) {
+                const float4 vs =
+                    *reinterpret_cast<const float4*>(p.v_scale + (b * p.h + j) * D + d0);
+                r.x *= vs.x;
+                r.y *= vs.y;
+                r.z *= vs.z;
+                r.w *= vs.w;
+            }
+            *reinterpret_cast<float4*>(orow + d0) = r;
         }
-        *reinterpret_cast<float4*>(orow + d0) = r;
     }
+}
+
+template <int D, int QB, int WAVES>
+void launch_shape(const ConsumerLaunch& a, const ConsumerParams& p, hipStream_t stream) {
+    constexpr int nq = 16 * QB * WAVES;   // queries per workgroup
+    const dim3 grid((unsigned)((a.used + nq - 1) / nq), (unsigned)a.h, (unsigned)a.B);
+    hipLaunchKernelGGL((consumer_kernel<D, QB, WAVES>), grid, dim3(64 * WAVES), 0, stream, p);
 }
 
 }  // namespace
@@ -310,14 +422,15 @@ hipError_t launch_consumer(const ConsumerLaunch& a, hipStream_t stream) {
     p.W = a.W;
     p.used = a.used;
     p.score_scale = (float)(1.4426950408889634 / std::sqrt((double)a.D));
+    // Shapes, measured: at D = 128, 8 waves x 2 column blocks (256 queries per workgroup,
+    // one workgroup per CU) when that still gives at least two workgroups per CU of the
+    // 256, else 4 waves x 1 block (64 queries, several workgroups per CU); at D = 64, 4 x 1.
     if (a.D == 64) {
-        constexpr int nq = 16 * consumer_waves<64>();
-        const dim3 grid((unsigned)((a.used + nq - 1) / nq), (unsigned)a.h, (unsigned)a.B);
-        hipLaunchKernelGGL((consumer_kernel<64>), grid, dim3(4 * nq), 0, stream, p);
+        launch_shape<64, 1, 4>(a, p, stream);
+    } else if ((a.used + 255) / 256 * a.h * a.B >= 512) {
+        launch_shape<128, 2, 8>(a, p, stream);
     } else {
-        constexpr int nq = 16 * consumer_waves<128>();
-        const dim3 grid((unsigned)((a.used + nq - 1) / nq), (unsigned)a.h, (unsigned)a.B);
-        hipLaunchKernelGGL((consumer_kernel<128>), grid, dim3(4 * nq), 0, stream, p);
+        launch_shape<128, 1, 4>(a, p, stream);
     }
     return hipGetLastError();
 }

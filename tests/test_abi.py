@@ -267,6 +267,11 @@ def test_consumer_validation(L):
     assert call(h=0) == EINVAL
     assert call(v=A + 4) == EALIGN
     assert L.ulp_consumer_attention(A, 0, A, A, A, None, 1, 128, 2, 64, 2, 128, A, None) == EINVAL
+    # one batch entry of k8 / v8 must stay below 2 GiB (32-bit offsets inside the kernel):
+    # S * h * D = 2^31 exactly is refused
+    S = 2 ** 31 // (64 * 128)
+    assert call(S=S, h=64, D=128, W=S // 64, used=S) == EINVAL
+    assert b"2 GiB" in L.ulp_last_error()
 
 
 def test_stats_with_mean_validation(L):

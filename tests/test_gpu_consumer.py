@@ -111,9 +111,12 @@ def test_mfma_consumer_within_fp8_bound(olib, wname):
 
 @pytest.mark.parametrize("P,L,H,D,used", [(2, 1, 2, 64, 1), (2, 33, 4, 128, 50),
                                           (4, 100, 8, 64, 257), (8, 40, 8, 128, 320),
-                                          (2, 96, 2, 128, 130)])
+                                          (2, 96, 2, 128, 130), (2, 4000, 32, 128, 7999)])
 def test_mfma_consumer_edges(olib, P, L, H, D, used):
-    """One live row, used below / at / just past a 64-row group, S not a multiple of 64."""
+    """One live row, used below / at / just past a 64-row group, S not a multiple of 64.
+    The last case has enough query tiles (2 x 16 heads x 32 tiles of 256 queries) for the
+    launcher's 256-query workgroups, with a partial last key tile, a last workgroup whose
+    waves end past `used` and past S."""
     w, d = grouped_inputs(small(B=2, P=P, L=L, H=H, D=D, dtype=torch.float16, used=used,
                                 scale_sequence=used, seed=used))
     vs = caller_v_scale(d, w)
@@ -131,3 +134,37 @@ def test_mfma_consumer_rejects_bad_arguments(olib):
         ulp.consumer_attention(q8, q8, v8, sc, sc, used=65)
     with pytest.raises(ValueError, match="v_scale"):
         ulp.consumer_attention(q8, q8, v8, sc, sc, used=64, v_scale=torch.ones(1, 2, 32, device=DEV))
+
+
+@pytest.mark.parametrize("wname,P,L,H,D,used", [
+    ("unaligned_padded_b2_p4_l1000_h16_d128_fp16", None, None, None, None, None),
+    ("batched_small_head_b4_p2_l2048_h24_d64_fp16", None, None, None, None, None),
+    ("edge", 2, 4000, 32, 128, 7999), ("edge", 4, 100, 8, 64, 257),
+    ("edge", 2, 33, 4, 128, 50)])
+def test_mfma_consumer_query_position_invariance(olib, wname, P, L, H, D, used):
+    """With no causal mask a query's output depends only on its own row and on its Q scale
+    group, not on where the row sits among the queries: reversing the live rows of the last
+    64-row group (one Q scale) must reverse their outputs bit for bit, and leave every other
+    row's bits alone.  The reversal moves queries into and out of the last, partly live,
+    wave of a workgroup, so any result that depends on a lane's neighbours or on which lanes
+    are active (an MFMA run with part of the wave switched off, say) shows here."""
+    if wname == "edge":
+        w, d = grouped_inputs(small(B=2, P=P, L=L, H=H, D=D, dtype=torch.float16, used=used,
+                                    scale_sequence=used, seed=used))
+    else:
+        w, d = grouped_inputs(W.BY_NAME[wname])
+    say(f"[mfma consumer position] {w.name}")
+    g = run_group(w, to_dev(d, w.P), w.aligned)
+    n = w.used or w.S
+    lo = (n - 1) // 64 * 64                      # first row of the last live 64-row group
+    rows = torch.arange(lo, n, device=DEV)
+    for p in range(w.P):
+        q8, k8, v8, qs, ks = g["outs"][p]
+        out = ulp.consumer_attention(q8, k8, v8, qs, ks, used=n)
+        q8r = q8.clone()
+        q8r[:, rows] = q8[:, rows.flip(0)]
+        outr = ulp.consumer_attention(q8r, k8, v8, qs, ks, used=n)
+        torch.cuda.synchronize()
+        assert torch.equal(outr[:, :lo].view(torch.int32), out[:, :lo].view(torch.int32)), p
+        assert torch.equal(outr[:, rows].view(torch.int32),
+                           out[:, rows.flip(0)].view(torch.int32)), (p, lo, n)
