@@ -205,22 +205,26 @@ void consumer_kernel(ConsumerParams p) {
     // or past the K range and read as zeros; V columns past Spad are pointed past the V
     // range (0x80000000) and read as zeros; the ranges end inside batch entry b.
     const uint32_t vbytes_b = (uint32_t)(D * vrow - j * p.spad);   // vg .. end of entry b
-    auto issue = [&](uint8_t* kd, uint8_t* vd, int64_t t0) {
-        const v4i krs = buffer_resource(kg + t0 * hD, (uint32_t)((p.used - t0) * hD));
-        const v4i vrs = buffer_resource(vg + t0, vbytes_b - (uint32_t)t0);
+    // Loads of the K tile of keys [tk, tk + KT) into kd and of the V tile of keys
+    // [tv, tv + KT) into vd, each only if asked for (k_on / v_on are uniform).
+    auto issue = [&](uint8_t* kd, int64_t tk, bool k_on, uint8_t* vd, int64_t tv, bool v_on) {
+        const v4i krs = buffer_resource(kg + tk * hD, (uint32_t)((p.used - tk) * hD));
+        const v4i vrs = buffer_resource(vg + tv, vbytes_b - (uint32_t)tv);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int c = wave + WAVES * i;
             if (c < NKC) {
+                if (!k_on) continue;
                 const int off = c * 1024 + 16 * lane;
                 const int slot = off / D, lp = k_piece<D>(slot, (off % D) / 16);
                 // LDS slot 16 kb + 4 q + r holds key 32 q + 4 kb + r of the tile
                 const int key = 32 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
                 buffer_load_lds16(krs, lds_address(kd + c * 1024), key * (int)hD + 16 * lp);
             } else {
+                if (!v_on) continue;
                 const int off = (c - NKC) * 1024 + 16 * lane;
                 const int row = off / KT, lp = v_piece(row, (off % KT) / 16);
-                const int vo = t0 + 16 * lp < p.spad ? row * (int)vrow + 16 * lp
+                const int vo = tv + 16 * lp < p.spad ? row * (int)vrow + 16 * lp
                                                      : (int)0x80000000;
                 buffer_load_lds16(vrs, lds_address(vd + (c - NKC) * 1024), vo);
             }
@@ -233,28 +237,13 @@ void consumer_kernel(ConsumerParams p) {
         const int64_t gi = t0 / 64 + (grp >> 1);
         return gi < p.W ? ksc[gi] : 1.0f;
     };
-    float ks_next = k_scale_of(0);
-    issue(tl.k[0], tl.v[0], 0);
-    lds_load_barrier();
 
-    // One tile: start the loads of the next pair (if `next`) into kd / vd, then compute from
-    // kl / vl; the loads complete by the barrier after the step.
-    // `last` (a compile-time tag) marks the final tile, the only one that can hold keys past
-    // `used`; the other tiles carry no masking code.
-    auto step = [&](auto last, const uint8_t* kl, const uint8_t* vl, uint8_t* kd, uint8_t* vd,
-                    int64_t t0, bool next) {
-        const float ks = ks_next;
-        if (next) {
-            ks_next = k_scale_of(t0 + KT);
-            issue(kd, vd, t0 + KT);
-        }
-        // S^T, 16 keys per MFMA: row i of block kb is key 32 (i / 4) + 4 kb + i % 4 of the
-        // tile, so the accumulator rows 4 grp + r of every block hold this lane's 32
-        // consecutive keys 32 grp + 4 kb + r.
-        // (The loads store key row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block
-        // kb reads 16 consecutive slots.)
-        // Each K fragment read from LDS feeds the MFMAs of all QB column blocks.
-        v4i s[QB][KB];
+    // S^T of one tile from its K tile kl, 16 keys per MFMA: row i of block kb is key
+    // 32 (i / 4) + 4 kb + i % 4 of the tile, so the accumulator rows 4 grp + r of every
+    // block hold this lane's 32 consecutive keys 32 grp + 4 kb + r.  (The loads store key
+    // row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block kb reads 16 consecutive
+    // slots.)  Each K fragment read from LDS feeds the MFMAs of all QB column blocks.
+    auto s_tile = [&](const uint8_t* kl, v4i (&s)[QB][KB]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -271,6 +260,16 @@ void consumer_kernel(ConsumerParams p) {
                                                                        0, 0, 0);
             }
         }
+    };
+
+    // Softmax of the tile starting at t0 from its dot products s: the running maximum and
+    // row sum move on, pw gets the packed E4M3 probabilities (scaled by 448), and alpha /
+    // resc say how the output sums must be rescaled before the tile's P.V is added (resc
+    // is false, uniformly over the wave, when no query's maximum moved).  `last` (a
+    // compile-time tag) marks the final tile, the only one that can hold keys past `used`;
+    // the other tiles carry no masking code.
+    auto softmax = [&](auto last, v4i (&s)[QB][KB], int64_t t0, float ks,
+                       uint32_t (&pw)[QB][KB], float (&alpha)[QB], bool (&resc)[QB]) {
         // The lane's keys lie in one 64-key K scale group, so its largest score is its
         // largest dot product times that scale.  The int32 dot products convert exactly;
         // only the last tile can hold keys past `used`, which become -inf (no maximum,
@@ -278,7 +277,6 @@ void consumer_kernel(ConsumerParams p) {
         // key 32 grp + i of the tile is live iff i < lim (compared against the constant i)
         const int lim = (int)min((int64_t)KT, p.used - t0) - 32 * grp;
         const float scl = t0 / 64 + (grp >> 1) < p.W ? qs * ks : 1.0f;
-        uint32_t pw[QB][KB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             float xf[KB][4];
@@ -320,18 +318,30 @@ void consumer_kernel(ConsumerParams p) {
             }
             psum = quad_sum(psum);
             // Rescale the running sums only when some query's maximum moved in this wave.
-            if (__builtin_amdgcn_ballot_w64(mnew != m[qb]) != 0) {
-                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-                lsum[qb] *= alpha;
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb) o[qb][cb] *= alpha;
+            resc[qb] = __builtin_amdgcn_ballot_w64(mnew != m[qb]) != 0;
+            alpha[qb] = 1.0f;
+            if (resc[qb]) {
+                alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);
+                lsum[qb] *= alpha[qb];
             }
             lsum[qb] += psum;
             m[qb] = mnew;
         }
-        // P^T fragment: the lane's 32 keys, byte 4 kb + r = key 32 grp + 4 kb + r, i.e. in
-        // key order; the V^T rows (channels) supply the same 32 consecutive keys.
-        // Each V fragment read from LDS feeds the MFMAs of all QB column blocks.
+    };
+    auto rescale = [&](const float (&alpha)[QB], const bool (&resc)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            if (resc[qb]) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) o[qb][cb] *= alpha[qb];
+            }
+    };
+
+    // O^T += V^T P^T for one tile from its V tile vl.  P^T fragment: the lane's 32 keys,
+    // byte 4 kb + r = key 32 grp + 4 kb + r, i.e. in key order; the V^T rows (channels)
+    // supply the same 32 consecutive keys.  Each V fragment read from LDS feeds the MFMAs
+    // of all QB column blocks.
+    auto pv_tile = [&](const uint8_t* vl, const uint32_t (&pw)[QB][KB]) {
         v8i pf[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -352,17 +362,32 @@ void consumer_kernel(ConsumerParams p) {
                     va, pf[qb], o[qb][cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
     };
+
+    // Tile by tile: the next tile's loads (into the other buffer) are in flight while this
+    // tile's products and softmax run; they complete by the barrier after it.
+    float ks_next = k_scale_of(0);
+    issue(tl.k[0], 0, true, tl.v[0], 0, true);
+    lds_load_barrier();
+    auto step = [&](auto last, int buf, int64_t t0, bool next) {
+        const float ks = ks_next;
+        if (next) {
+            ks_next = k_scale_of(t0 + KT);
+            issue(tl.k[buf ^ 1], t0 + KT, true, tl.v[buf ^ 1], t0 + KT, true);
+        }
+        v4i s[QB][KB];
+        s_tile(tl.k[buf], s);
+        uint32_t pw[QB][KB];
+        float alpha[QB];
+        bool resc[QB];
+        softmax(last, s, t0, ks, pw, alpha, resc);
+        rescale(alpha, resc);
+        pv_tile(tl.v[buf], pw);
+    };
     for (int64_t kt = 0; kt + 1 < ntiles; ++kt) {
-        const int buf = (int)(kt & 1);
-        step(std::false_type{}, tl.k[buf], tl.v[buf], tl.k[buf ^ 1], tl.v[buf ^ 1], kt * KT,
-             true);
+        step(std::false_type{}, (int)(kt & 1), kt * KT, true);
         lds_load_barrier();   // the next pair has landed; this one is no longer read
     }
-    {
-        const int buf = (int)((ntiles - 1) & 1);
-        step(std::true_type{}, tl.k[buf], tl.v[buf], tl.k[buf ^ 1], tl.v[buf ^ 1],
-             (ntiles - 1) * KT, false);
-    }
+    step(std::true_type{}, (int)((ntiles - 1) & 1), (ntiles - 1) * KT, false);
     // The last tile's results are used only by the lanes of live queries (the branch
     // below).  MFMAs need every lane of the wave, so they must not run inside that branch:
     // an opaque use of every accumulator here, where all lanes are active, keeps the
