@@ -168,3 +168,26 @@ def test_mfma_consumer_query_position_invariance(olib, wname, P, L, H, D, used):
         assert torch.equal(outr[:, :lo].view(torch.int32), out[:, :lo].view(torch.int32)), p
         assert torch.equal(outr[:, rows].view(torch.int32),
                            out[:, rows.flip(0)].view(torch.int32)), (p, lo, n)
+
+
+def test_mfma_consumer_launch_shape_invariance(olib):
+    """Each query's output is computed with the same operations in the same order whatever
+    workgroup shape the launcher picks: run over 16 heads x 2 batch entries the launch takes
+    256-query workgroups (8 waves of two 16-query blocks); head 3 alone, copied out, is too
+    small a launch for that and takes 64-query ones (4 waves of one block).  The two must
+    give the same bits for that head."""
+    w, d = grouped_inputs(small(B=2, P=2, L=2000, H=32, D=128, dtype=torch.float16,
+                                used=3999, scale_sequence=3999, seed=11))
+    say(f"[mfma consumer shapes] {w.name}")
+    g = run_group(w, to_dev(d, w.P), w.aligned)
+    n = w.used
+    assert (n + 255) // 256 * w.h * w.B >= 512          # the 256-query shape
+    assert (n + 255) // 256 * 1 * w.B < 512              # one head: the 64-query shape
+    q8, k8, v8, qs, ks = g["outs"][1]
+    full = ulp.consumer_attention(q8, k8, v8, qs, ks, used=n)
+    j = 3
+    one = ulp.consumer_attention(q8[:, :, j:j + 1].contiguous(), k8[:, :, j:j + 1].contiguous(),
+                                 v8[:, :, j:j + 1].contiguous(), qs[:, j:j + 1].contiguous(),
+                                 ks[:, j:j + 1].contiguous(), used=n)
+    torch.cuda.synchronize()
+    assert torch.equal(one[:, :, 0].view(torch.int32), full[:, :, j].view(torch.int32))
