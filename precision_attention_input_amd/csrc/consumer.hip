@@ -13,12 +13,12 @@
 // Smooth K needs no correction: removing a per-channel mean from every key shifts all scores
 // of a query by the same amount.
 //
-// Work decomposition: a 256-thread workgroup owns 64 query rows of one (b, head) -- one Q
-// scale group -- and each wave 16 of them.  Key tiles of 128 rows (two K scale groups) and
-// the matching 128 columns of v8 are copied with coalesced 16-byte loads into
-// double-buffered LDS tiles shared by the four waves; the next tile's loads are in flight
-// while the current one is computed.  Both products are computed transposed, so that every
-// per-query quantity lives in the lanes of that query's column:
+// Work decomposition: a workgroup of WAVES waves owns WAVES x QB x 16 query rows of one
+// (b, head); a wave owns QB column blocks of 16 queries, all in one Q scale group.  Key
+// tiles of 128 rows (two K scale groups) and the matching 128 columns of v8 are loaded from
+// memory straight into double-buffered LDS tiles shared by the waves; the next tile's loads
+// are in flight while the current one is computed.  Both products are computed transposed,
+// so that every per-query quantity lives in the lanes of that query's column:
 //   S^T[key, q] = K . Q^T   (A = 16 keys x 64 channels of k8, B = 64 channels x 16 queries)
 //   O^T[d, q]  += V^T . P^T (A = 16 channels x 128 keys of v8, B = 128 keys x 16 queries)
 // Lane l of an MFMA operand holds row / column l % 16 and the bytes of lane group l / 16;
@@ -32,8 +32,8 @@
 // then the P.V product's B operand in key order, the V^T fragment is 32 consecutive bytes
 // of a channel row, and each lane's keys share one K scale group.  No data moves between
 // lanes except the max / sum reductions over the four lanes of a query.  The permutation is
-// applied once, when a K row is stored in LDS (slot 16 kb + 4 q + r for key 32 q + 4 kb + r),
-// so every fragment read covers 16 consecutive padded rows.
+// applied once, when a K row lands in LDS (slot 16 kb + 4 q + r for key 32 q + 4 kb + r),
+// so every fragment read covers 16 consecutive rows.
 #include <cmath>
 #include <type_traits>
 
