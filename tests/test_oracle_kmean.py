@@ -69,6 +69,24 @@ def test_k_mean_against_exact_sum(olib, shape, dtype):
         assert torch.equal(md.view(torch.int16), ed.view(torch.int16))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_k_mean_wide_range_against_exact_sum(olib, dtype):
+    """Magnitudes spread over 2^-10 .. 2^10 with both signs: a binary32 running sum or a
+    binary32 division loses bits here, while a binary64 sum of a few hundred such values is
+    still exact, so the result must equal the exactly rounded one bit for bit."""
+    P, B, L, H, D = 4, 1, 75, 4, 64
+    rng = torch.Generator().manual_seed(11)
+    mag = torch.exp2(torch.randint(-10, 11, (P, B, L, H, D), generator=rng).float())
+    frac = 1 + torch.rand(P, B, L, H, D, generator=rng)
+    sign = torch.randint(0, 2, (P, B, L, H, D), generator=rng).float() * 2 - 1
+    ks = (sign * mag * frac).to(dtype)
+    for used in (P * L, 211, 3):
+        mf, md = oracle.k_mean(ks, used_sequence=used)
+        ef, ed = exact_mean_bits(ks, used, dtype)
+        assert torch.equal(mf.view(torch.int32), ef.view(torch.int32)), used
+        assert torch.equal(md.view(torch.int16), ed.view(torch.int16)), used
+
+
 def test_k_mean_matches_workload_recipe(olib):
     """The workloads' k_mean_global (chunked float64 sum) is the same definition."""
     for w in (small(P=4, L=100, H=4, D=64, used=333, seed=3),

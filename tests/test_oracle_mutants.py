@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+import test_oracle_kmean as kmn
 import test_oracle_pins as pins
 import test_oracle_pipeline as pipe
 import test_oracle_vscale as vsc
@@ -61,6 +62,17 @@ MUTANTS = {
                            "vf = vf / v_scale[(b * H + j) * D + d];"),
     "v_scale_ignored": ("if (v_scale) vf = vf / v_scale[(b * H + hh) * D + d];", ""),
     "minmax_keeps_negative_zero": ("if (v == 0.0f) v = 0.0f;", ""),
+    "kmean_divides_by_rows": ("float m = (float)(sum / (double)u);",
+                              "float m = (float)(sum / (double)S);"),
+    "kmean_sums_padding": ("for (int64_t t = 0; t < u; t++) {", "for (int64_t t = 0; t < S; t++) {"),
+    "kmean_rank_major_rows": ("int64_t r = t / L, l = t % L;", "int64_t r = t % P, l = t / P;"),
+    "kmean_binary32_sum": ("double sum = 0.0;", "float sum = 0.0f;"),
+    "kmean_binary32_divide": ("float m = (float)(sum / (double)u);",
+                              "float m = (float)sum / (float)u;"),
+    "bf16_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
+                       "return (uint16_t)(u >> 16);"),
+    "bf16_ties_away": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
+                       "return (uint16_t)((u + 0x8000u) >> 16);"),
 }
 
 
@@ -79,6 +91,15 @@ def battery(first_failure_only: bool = False):
         ("only_partial_live", lambda: pipe.test_only_partial_live_group_changes(None, 195)),
         ("v_scale_hand", lambda: vsc.test_hand_worked_values(None)),
         ("v_scale_definition", lambda: vsc.test_v_scale_matches_definition(None, vsc.CASES[0])),
+        ("k_mean_recipe", lambda: kmn.test_k_mean_against_exact_sum(None, (4, 2, 33, 4, 64),
+                                                                    torch.bfloat16)),
+        ("k_mean_recipe_fp16", lambda: kmn.test_k_mean_against_exact_sum(None, (2, 1, 100, 2, 64),
+                                                                         torch.float16)),
+        ("k_mean_wide_range",
+         lambda: kmn.test_k_mean_wide_range_against_exact_sum(None, torch.bfloat16)),
+        ("k_mean_workload", lambda: kmn.test_k_mean_matches_workload_recipe(None)),
+        ("dtype_rounding_bf16",
+         lambda: kmn.test_dtype_rounding_matches_library(None, torch.bfloat16)),
     ]
     for w in [small(B=2, P=4, L=100, H=8, D=64, used=301, scale_sequence=301, seed=1),
               small(P=2, L=65, H=4, D=128, dtype=torch.float16, used=100, seed=2),
