@@ -295,7 +295,16 @@ def consumer_bench(args, w, d, dev):
 
     for _ in range(args.warmup):
         run()
+    # Small launches finish before the GPU's clocks have risen: keep warming up until about
+    # --warm-ms of launches have run.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.warm_ms > 0:
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(min(2000, int(args.warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
+            run()
     torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
@@ -331,6 +340,9 @@ def main():
                     help="seconds of repetitions behind the CPU oracle's pack+unpack figure "
                          "(the amax and single-thread figures take half and a quarter of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-ms", type=float, default=300.0,
+                    help="with --consumer: extra warm-up launches until about this many ms "
+                         "of them have run (0: only --warmup)")
     ap.add_argument("--consumer", action="store_true",
                     help="time the MFMA consumer check (INT8 Q.K, FP8 P.V attention over every "
                          "destination's unpacked tensors) instead of the path; prints its own "

@@ -60,24 +60,34 @@ def quantized_attention(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries
 
 
 def fp8_probability_bound(q8, k8, v8, q_scale, k_scale, *, b: int, j: int, queries,
-                          used: int, v_scale_row=None):
+                          used: int, v_scale_row=None, exponent_error: float = 0.0):
     """(out, bound) [len(queries), D]: the attention above and a per-element bound on how far
-    a consumer that rounds each probability to E4M3 (after scaling it by 448, with any
-    running maximum m_run <= the row maximum) may land from it.  Rounding to E4M3 moves a
-    value by at most 2^-4 of itself in the normal range and by at most 2^-10 (half the
-    smallest subnormal step) below it, i.e. a probability p by at most
-    max(2^-4 p, 2^-10 / 448) <= max(2^-4 p, 2^-18) in units of the row maximum; scaling by
-    exp2(m_run - max) <= 1 only shrinks that.  So
-        |out_fp8 - out| <= sum_t max(2^-4 p_t, 2^-18) |v_t| / sum_t p_t,
-    plus binary32 arithmetic (scores, exponentials, FP32 accumulation of up to `used`
-    terms), held to 1e-3 of sum_t p_t |v_t| / sum_t p_t."""
+    a consumer may land from it that rounds each probability to E4M3 (after scaling it by
+    448, with any running maximum m_run <= the row maximum), normalizes each row by the sum
+    of its rounded probabilities, and computes each exponent argument (log2 units) to
+    within `exponent_error` of score * log2(e) - m_run.
+
+    In units of the row maximum, the exponent moves a probability p by a factor within
+    2^(+-exponent_error); rounding to E4M3 then moves it by at most 2^-4 of itself in the
+    normal range and by at most 2^-10 (half the smallest subnormal step) below it, i.e. by
+    at most max(2^-4 p, 2^-10 / 448) <= max(2^-4 p, 2^-18); scaling by
+    exp2(m_run - max) <= 1 only shrinks that.  So a rounded probability q_t lies within
+        E_t = 2^x max(2^-4 p_t, 2^-18) + (2^x - 1) p_t        (x = exponent_error)
+    of p_t.  As sum_t p_t (v_t - out) = 0, the consumer's sum_t q_t v_t / sum_t q_t differs
+    from out by sum_t (q_t - p_t)(v_t - out) / sum_t q_t, hence
+        |out_fp8 - out| <= sum_t E_t |v_t - out| / (sum_t p_t - sum_t E_t)
+    (sum_t p_t >= 1, the maximum's term; the bound is infinite where the denominator is not
+    positive), plus binary32 arithmetic (FP32 accumulation of up to `used` terms, the
+    rescales, the final division), held to 1e-3 of sum_t p_t |v_t| / sum_t p_t."""
     p, l = _probabilities(q8, k8, q_scale, k_scale, b, j, queries, used)
     v = _values(v8, b, j, used, v_scale_row)
     out = (p @ v) / l
-    av = v.abs()
-    bound = (torch.maximum(p * 2.0 ** -4, torch.full_like(p, 2.0 ** -18)) @ av) / l \
-        + 1e-3 * (p @ av) / l
-    return out, bound
+    grow = 2.0 ** exponent_error
+    e = grow * torch.maximum(p * 2.0 ** -4, torch.full_like(p, 2.0 ** -18)) + (grow - 1.0) * p
+    den = l - e.sum(dim=-1, keepdim=True)
+    num = torch.stack([e[i] @ (v - out[i]).abs() for i in range(len(out))])   # [nq, D]
+    bound = torch.where(den > 0, num / den.clamp_min(1e-300), torch.full_like(num, float("inf")))
+    return out, bound + 1e-3 * (p @ v.abs()) / l
 
 
 def reference_attention(Q, K, V, *, b: int, head: int, queries, used: int) -> torch.Tensor:

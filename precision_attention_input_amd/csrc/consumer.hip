@@ -10,6 +10,9 @@
 // with the INT8 dot products on gfx950's v_mfma_i32_16x16x64_i8 (exact int32) and the P.V
 // product on v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 operands, unit block scales), P
 // quantized to E4M3 after scaling by 448 (the largest E4M3 value), as an FP8 consumer does.
+// Each row is normalized by the sum of its rounded probabilities, formed on the matrix
+// cores in the same products as the output (a Sage consumer sums the unrounded ones in
+// FP32; either is a valid normalization of the rounded weights).
 // Smooth K needs no correction: removing a per-channel mean from every key shifts all scores
 // of a query by the same amount.
 //
@@ -31,7 +34,7 @@
 // keys 32 g + [0, 32) (byte 4 kb + r = key 32 g + 4 kb + r): the lane's packed P bytes are
 // then the P.V product's B operand in key order, the V^T fragment is 32 consecutive bytes
 // of a channel row, and each lane's keys share one K scale group.  No data moves between
-// lanes except the max / sum reductions over the four lanes of a query.  The permutation is
+// lanes except the max reduction over the four lanes of a query.  The permutation is
 // applied once, when a K row lands in LDS (slot 16 kb + 4 q + r for key 32 q + 4 kb + r),
 // so every fragment read covers 16 consecutive rows.
 #include <cmath>
@@ -54,6 +57,13 @@ constexpr int kConsumerKeys = 128;   // keys per LDS tile: one P.V MFMA per chan
 // The launcher picks the shape (see launch_consumer).
 constexpr int kUnitScale = 127;      // E8M0 block scale 2^0
 constexpr float kLog2_448 = 8.807354922057604f;   // log2(448)
+// The S^T accumulators start at the bit pattern of 1.5 * 2^23 instead of 0.  Binary32
+// values in [2^23, 2^24) are the integers, one per bit pattern, so for any dot product d
+// with |d| < 2^22 (127 * 127 * D <= 2064512 here) the accumulator's bits read as a float
+// are exactly 1.5 * 2^23 + d: the scores need no integer-to-float conversion.
+constexpr int kDotBias = 0x4B400000;
+constexpr float kDotBiasF = 12582912.0f;
+constexpr int kE4M3One = 0x38;       // E4M3 encoding of 1.0
 
 struct ConsumerParams {
     const int8_t *q8, *k8;
@@ -65,11 +75,11 @@ struct ConsumerParams {
 };
 
 
-// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's lanes), left in all
-// four, with gfx950's lane-swap instructions: v_permlane16_swap exchanges rows 1 and 3 of one
+// Max over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query's lanes), left in all four,
+// with gfx950's lane-swap instructions: v_permlane16_swap exchanges rows 1 and 3 of one
 // register with rows 0 and 2 of another, v_permlane32_swap the upper half of one with the
 // lower half of another; both operands are copies of v, so each result lane meets its
-// partner's value.  No LDS traffic.  The sum is (r0 + r1) + (r2 + r3) in every lane.
+// partner's value.  No LDS traffic.
 __device__ __forceinline__ float quad_max(float v) {
     const unsigned u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -77,14 +87,6 @@ __device__ __forceinline__ float quad_max(float v) {
     const unsigned w = __float_as_uint(v);
     const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float v) {
-    const unsigned u = __float_as_uint(v);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const unsigned w = __float_as_uint(v);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // LDS tiles: KT key slots x D channels of k8 and D channels x KT keys of v8, unpadded.  The
@@ -184,14 +186,17 @@ void consumer_kernel(ConsumerParams p) {
     const float qs = p.q_scale[(b * p.h + j) * p.W + qg] * p.score_scale;
     const float* ksc = p.k_scale + (b * p.h + j) * p.W;
 
-    v4f o[QB][CB];
-    float m[QB], lsum[QB];
+    // o: the output sums O^T; ls: the row sums, one more O^T block whose 16 "channels" are
+    // all E4M3 ones, so every element of ls[qb] is the sum of the rounded probabilities of
+    // the lane's query; m: the running maximum (log2 units).
+    v4f o[QB][CB], ls[QB];
+    float m[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) o[qb][cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        ls[qb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         m[qb] = -__builtin_inff();
-        lsum[qb] = 0.0f;
     }
 
     const int64_t ntiles = (p.used + KT - 1) / KT;
@@ -205,28 +210,44 @@ void consumer_kernel(ConsumerParams p) {
     // or past the K range and read as zeros; V columns past Spad are pointed past the V
     // range (0x80000000) and read as zeros; the ranges end inside batch entry b.
     const uint32_t vbytes_b = (uint32_t)(D * vrow - j * p.spad);   // vg .. end of entry b
-    // Loads of the K tile of keys [tk, tk + KT) into kd and of the V tile of keys
-    // [tv, tv + KT) into vd, each only if asked for (k_on / v_on are uniform).
-    auto issue = [&](uint8_t* kd, int64_t tk, bool k_on, uint8_t* vd, int64_t tv, bool v_on) {
+    // The lane's part of each of the wave's CPW pieces, the same for every tile: the byte
+    // offset it loads from, relative to the tile's first key (K) or column (V), and for V
+    // the tile column it starts at.
+    int ld_off[CPW], ld_col[CPW];
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+        const int c = wave + WAVES * i;
+        if (c < NKC) {
+            const int off = c * 1024 + 16 * lane;
+            const int slot = off / D, lp = k_piece<D>(slot, (off % D) / 16);
+            // LDS slot 16 kb + 4 q + r holds key 32 q + 4 kb + r of the tile
+            const int key = 32 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
+            ld_off[i] = key * (int)hD + 16 * lp;
+            ld_col[i] = 0;
+        } else {
+            const int off = (c - NKC) * 1024 + 16 * lane;
+            const int row = off / KT, lp = v_piece(row, (off % KT) / 16);
+            ld_off[i] = row * (int)vrow + 16 * lp;
+            ld_col[i] = 16 * lp;
+        }
+    }
+    const uint32_t lds_k = lds_address(tl.k[0]), lds_v = lds_address(tl.v[0]);
+    // Loads of the K tile of keys [tk, tk + KT) into K buffer kbuf and of the V tile of
+    // keys [tv, tv + KT) into V buffer vbuf, each only if asked for (k_on / v_on are
+    // uniform).
+    auto issue = [&](int kbuf, int64_t tk, bool k_on, int vbuf, int64_t tv, bool v_on) {
         const v4i krs = buffer_resource(kg + tk * hD, (uint32_t)((p.used - tk) * hD));
         const v4i vrs = buffer_resource(vg + tv, vbytes_b - (uint32_t)tv);
+        const int vlive = (int)min((int64_t)KT, p.spad - tv);   // columns before Spad
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int c = wave + WAVES * i;
             if (c < NKC) {
-                if (!k_on) continue;
-                const int off = c * 1024 + 16 * lane;
-                const int slot = off / D, lp = k_piece<D>(slot, (off % D) / 16);
-                // LDS slot 16 kb + 4 q + r holds key 32 q + 4 kb + r of the tile
-                const int key = 32 * ((slot & 15) >> 2) + 4 * (slot >> 4) + (slot & 3);
-                buffer_load_lds16(krs, lds_address(kd + c * 1024), key * (int)hD + 16 * lp);
-            } else {
-                if (!v_on) continue;
-                const int off = (c - NKC) * 1024 + 16 * lane;
-                const int row = off / KT, lp = v_piece(row, (off % KT) / 16);
-                const int vo = tv + 16 * lp < p.spad ? row * (int)vrow + 16 * lp
-                                                     : (int)0x80000000;
-                buffer_load_lds16(vrs, lds_address(vd + (c - NKC) * 1024), vo);
+                if (k_on)
+                    buffer_load_lds16(krs, lds_k + kbuf * T::KBYTES + c * 1024, ld_off[i]);
+            } else if (v_on) {
+                buffer_load_lds16(vrs, lds_v + vbuf * T::VBYTES + (c - NKC) * 1024,
+                                  ld_col[i] < vlive ? ld_off[i] : (int)0x80000000);
             }
         }
     };
@@ -242,12 +263,14 @@ void consumer_kernel(ConsumerParams p) {
     // 32 (i / 4) + 4 kb + i % 4 of the tile, so the accumulator rows 4 grp + r of every
     // block hold this lane's 32 consecutive keys 32 grp + 4 kb + r.  (The loads store key
     // row 32 q + 4 kb + r in LDS slot 16 kb + 4 q + r, so block kb reads 16 consecutive
-    // slots.)  Each K fragment read from LDS feeds the MFMAs of all QB column blocks.
+    // slots.)  Each K fragment read from LDS feeds the MFMAs of all QB column blocks.  The
+    // sums start from kDotBias.
     auto s_tile = [&](const uint8_t* kl, v4i (&s)[QB][KB]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb] = v4i{0, 0, 0, 0};
+            for (int qb = 0; qb < QB; ++qb)
+                s[qb][kb] = v4i{kDotBias, kDotBias, kDotBias, kDotBias};
             const int slot = 16 * kb + col;
             const uint8_t* krow = kl + slot * D;
 #pragma unroll
@@ -262,18 +285,18 @@ void consumer_kernel(ConsumerParams p) {
         }
     };
 
-    // Softmax of the tile starting at t0 from its dot products s: the running maximum and
-    // row sum move on, pw gets the packed E4M3 probabilities (scaled by 448), and alpha /
-    // resc say how the output sums must be rescaled before the tile's P.V is added (resc
-    // is false, uniformly over the wave, when no query's maximum moved).  `last` (a
+    // Softmax of the tile starting at t0 from its biased dot products s: the running maximum
+    // moves on, pw gets the packed E4M3 probabilities (scaled by 448), and alpha / resc say
+    // how the output and row sums must be rescaled before the tile's P.V is added (resc is
+    // false, uniformly over the wave, when no query's maximum moved).  `last` (a
     // compile-time tag) marks the final tile, the only one that can hold keys past `used`;
     // the other tiles carry no masking code.
     auto softmax = [&](auto last, v4i (&s)[QB][KB], int64_t t0, float ks,
                        uint32_t (&pw)[QB][KB], float (&alpha)[QB], bool (&resc)[QB]) {
         // The lane's keys lie in one 64-key K scale group, so its largest score is its
-        // largest dot product times that scale.  The int32 dot products convert exactly;
-        // only the last tile can hold keys past `used`, which become -inf (no maximum,
-        // probability 0).
+        // largest dot product times that scale.  xf = 1.5 * 2^23 + dot exactly (kDotBias),
+        // ordered as the dot products are; only the last tile can hold keys past `used`,
+        // which become -inf (no maximum, probability 0).
         // key 32 grp + i of the tile is live iff i < lim (compared against the constant i)
         const int lim = (int)min((int64_t)KT, p.used - t0) - 32 * grp;
         const float scl = t0 / 64 + (grp >> 1) < p.W ? qs * ks : 1.0f;
@@ -283,7 +306,7 @@ void consumer_kernel(ConsumerParams p) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xf[kb][r] = (float)s[qb][kb][r];
+                for (int r = 0; r < 4; ++r) xf[kb][r] = __int_as_float(s[qb][kb][r]);
             if constexpr (decltype(last)::value) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
@@ -296,35 +319,33 @@ void consumer_kernel(ConsumerParams p) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) gmax = fmaxf(gmax, xf[kb][r]);
-            float tmax = gmax * scl;
+            float tmax = (gmax - kDotBiasF) * scl;   // the subtraction is exact
             tmax = quad_max(tmax);
             const float mnew = fmaxf(m[qb], tmax);   // finite: key t0 < used is live
-            // 448 p = exp2(score - mnew + log2(448)), one fma and one exp2 per key; the row
-            // sum is kept in the same 448-scaled units.  The values stay at or below 448 (up
-            // to the exp2 error), so the E4M3 conversion needs no clamp.
-            const float moff = mnew - kLog2_448;
-            float psum = 0.0f;
+            // 448 p = exp2(score - mnew + log2(448)) = exp2(xf * scl - moff), one fma and one
+            // exp2 per key, with the bias folded into moff (rounded once: the exponent of
+            // every key of the lane is off by at most half an ulp of moff, about
+            // 2^-24 * 1.5 * 2^23 * scl).  The values stay at or below 448 (up to that and
+            // the exp2 error), so the E4M3 conversion needs no clamp.
+            const float moff = __builtin_fmaf(kDotBiasF, scl, mnew - kLog2_448);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 float pr[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                for (int r = 0; r < 4; ++r)
                     pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(xf[kb][r], scl, -moff));
-                    psum += pr[r];
-                }
-                int w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], 0, false);
+                // the first conversion writes the low half and keeps the high half of its
+                // last operand, which the second overwrites: any bits do (an empty asm
+                // defines them without an instruction; a constant would cost a move)
+                int w;
+                asm volatile("" : "=v"(w));
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[0], pr[1], w, false);
                 w = __builtin_amdgcn_cvt_pk_fp8_f32(pr[2], pr[3], w, true);
                 pw[qb][kb] = (uint32_t)w;
             }
-            psum = quad_sum(psum);
             // Rescale the running sums only when some query's maximum moved in this wave.
             resc[qb] = __builtin_amdgcn_ballot_w64(mnew != m[qb]) != 0;
-            alpha[qb] = 1.0f;
-            if (resc[qb]) {
-                alpha[qb] = __builtin_amdgcn_exp2f(m[qb] - mnew);
-                lsum[qb] *= alpha[qb];
-            }
-            lsum[qb] += psum;
+            alpha[qb] = resc[qb] ? __builtin_amdgcn_exp2f(m[qb] - mnew) : 1.0f;
             m[qb] = mnew;
         }
     };
@@ -334,19 +355,22 @@ void consumer_kernel(ConsumerParams p) {
             if (resc[qb]) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) o[qb][cb] *= alpha[qb];
+                ls[qb] *= alpha[qb];
             }
     };
 
     // O^T += V^T P^T for one tile from its V tile vl.  P^T fragment: the lane's 32 keys,
     // byte 4 kb + r = key 32 grp + 4 kb + r, i.e. in key order; the V^T rows (channels)
     // supply the same 32 consecutive keys.  Each V fragment read from LDS feeds the MFMAs
-    // of all QB column blocks.
+    // of all QB column blocks.  One more MFMA per column block, with an A operand of E4M3
+    // ones, adds the rounded probabilities of each query to its row sum.
     auto pv_tile = [&](const uint8_t* vl, const uint32_t (&pw)[QB][KB]) {
         v8i pf[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
             pf[qb] = v8i{(int)pw[qb][0], (int)pw[qb][1], (int)pw[qb][2], (int)pw[qb][3],
                          (int)pw[qb][4], (int)pw[qb][5], (int)pw[qb][6], (int)pw[qb][7]};
+        v8i vas[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const int row = 16 * cb + col;
@@ -354,25 +378,39 @@ void consumer_kernel(ConsumerParams p) {
             const uint4 va0 = *reinterpret_cast<const uint4*>(vr + 16 * v_piece(row, 2 * grp));
             const uint4 va1 =
                 *reinterpret_cast<const uint4*>(vr + 16 * v_piece(row, 2 * grp + 1));
-            const v8i va = {(int)va0.x, (int)va0.y, (int)va0.z, (int)va0.w,
-                            (int)va1.x, (int)va1.y, (int)va1.z, (int)va1.w};
+            vas[cb] = v8i{(int)va0.x, (int)va0.y, (int)va0.z, (int)va0.w,
+                          (int)va1.x, (int)va1.y, (int)va1.z, (int)va1.w};
+        }
+        // with eight waves, all of the tile's V fragment reads are issued before its first
+        // P.V product (measured: 1-2 % faster); the smaller shapes leave the order to the
+        // compiler
+        if constexpr (WAVES == 8) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const v8i va = vas[cb];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
                 o[qb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     va, pf[qb], o[qb][cb], 0, 0, 0, kUnitScale, 0, kUnitScale);
         }
+        constexpr int ones4 = kE4M3One * 0x01010101;
+        const v8i ones = {ones4, ones4, ones4, ones4, ones4, ones4, ones4, ones4};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            ls[qb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                ones, pf[qb], ls[qb], 0, 0, 0, kUnitScale, 0, kUnitScale);
     };
 
     // Tile by tile: the next tile's loads (into the other buffer) are in flight while this
     // tile's products and softmax run; they complete by the barrier after it.
     float ks_next = k_scale_of(0);
-    issue(tl.k[0], 0, true, tl.v[0], 0, true);
+    issue(0, 0, true, 0, 0, true);
     lds_load_barrier();
     auto step = [&](auto last, int buf, int64_t t0, bool next) {
         const float ks = ks_next;
         if (next) {
             ks_next = k_scale_of(t0 + KT);
-            issue(tl.k[buf ^ 1], t0 + KT, true, tl.v[buf ^ 1], t0 + KT, true);
+            issue(buf ^ 1, t0 + KT, true, buf ^ 1, t0 + KT, true);
         }
         v4i s[QB][KB];
         s_tile(tl.k[buf], s);
@@ -396,14 +434,14 @@ void consumer_kernel(ConsumerParams p) {
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(o[qb][cb]));
-        asm volatile("" : "+v"(lsum[qb]));
+        asm volatile("" : "+v"(ls[qb]));
     }
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int64_t qi = qw + 16 * qb + col;
         if (qi >= p.used) continue;
-        const float inv = 1.0f / lsum[qb];         // lsum is in 448-scaled units
+        const float inv = 1.0f / ls[qb][0];        // the row sum, in 448-scaled units
         float* orow = p.out + (b * p.used + qi) * hD + j * D;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {

@@ -5,6 +5,8 @@ heads and query rows), with and without a caller V scale.  Bounds and their rati
 those of tests/test_oracle_consumer.py."""
 from __future__ import annotations
 
+import math
+
 import pytest
 import torch
 
@@ -58,6 +60,19 @@ def test_consumer_on_gpu_outputs(olib, wname):
 # sqrt(1 - r^2) (a vector within r |ref_in| of ref_in, r < 1, makes at most that angle).
 # How far exact itself lies from ref_in is the input quantization, which
 # test_consumer_on_gpu_outputs holds to COS / REL.
+def mfma_exponent_error(qs, ks, b: int, j: int, D: int) -> float:
+    """How far (log2 units) the MFMA kernel's exponent arguments may lie from the exact
+    score * log2(e) - running maximum.  The kernel reads its dot products biased by
+    1.5 * 2^23 and folds the bias into the offset 1.5 * 2^23 * scl + m - log2(448), which
+    it rounds once: half an ulp of at most (1.5 * 2^23 + 127^2 D) scl + 9, where
+    scl = q_scale * k_scale * log2(e) / sqrt(D) <= the largest such product of the head.
+    scl itself carries three binary32 roundings, a relative 3 * 2^-24 on
+    |dot * scl| <= 127^2 D scl; the fma and the exp2 each round on arguments of magnitude
+    up to a few hundred.  Taken here as a full ulp of the sum, with room to spare."""
+    scl = float(qs[b, j].max()) * float(ks[b, j].max()) * math.log2(math.e) / math.sqrt(D)
+    return 2.0 ** -23 * ((1.5 * 2 ** 23 + 4 * 127 ** 2 * D) * scl + 256)
+
+
 def _check_mfma_consumer(w, d, g, vs, dests, heads_of, nq, label):
     used = w.used or w.S
     qsel = sorted(set(list(range(0, used, max(1, used // nq))) + [used - 1, used // 2]))
@@ -73,8 +88,10 @@ def _check_mfma_consumer(w, d, g, vs, dests, heads_of, nq, label):
             for j in heads_of(p):
                 hh = p * w.h + j
                 row = None if vs is None else vs[b, hh]
+                xerr = mfma_exponent_error(c8[3], c8[4], b, j, q8.shape[-1])
                 ref, bound = consumer.fp8_probability_bound(*c8, b=b, j=j, queries=qsel,
-                                                            used=used, v_scale_row=row)
+                                                            used=used, v_scale_row=row,
+                                                            exponent_error=xerr)
                 got = out[b, qsel, j].double()
                 ratio = ((got - ref).abs() / bound).max().item()
                 assert ratio <= 1.0, f"{label}: dest {p} b {b} head {j}: error/bound {ratio}"
