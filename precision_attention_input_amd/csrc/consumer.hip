@@ -154,6 +154,7 @@ void consumer_kernel(ConsumerParams p) {
     constexpr int NQW = 16 * QB;               // queries per wave
     constexpr int NQ = NQW * WAVES;            // queries per workgroup
     static_assert(64 % NQW == 0, "a wave's queries share one Q scale group");
+    static_assert(127 * 127 * D < (1 << 22), "biased dot products stay in [2^23, 2^24)");
     // global -> LDS copy of one tile pair in 1 KB pieces, one wave instruction each
     constexpr int NKC = KT * D / 1024, NVC = D * KT / 1024;
     constexpr int CPW = (NKC + NVC) / WAVES;   // pieces per wave
