@@ -208,3 +208,38 @@ def test_mfma_consumer_launch_shape_invariance(olib):
                                  ks[:, j:j + 1].contiguous(), used=n)
     torch.cuda.synchronize()
     assert torch.equal(one[:, :, 0].view(torch.int32), full[:, :, j].view(torch.int32))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("scale", [1e-3, 3e-2])
+def test_mfma_consumer_extreme_dot_products(olib, D, scale):
+    """Q and K codes of +-127 in whole rows, so that the dot products reach +-127^2 D, the
+    ends of the range the kernel's biased accumulators must hold exactly; a small scale
+    gives a flat softmax, a large one a peaked one.  Held to the same FP8 bound."""
+    g = torch.Generator().manual_seed(D + int(scale * 1e4))
+    B, h, S = 1, 2, 300
+    sign = lambda n: torch.randint(0, 2, (n,), generator=g) * 2 - 1
+    q8 = (127 * sign(B * S * h)).view(B, S, h, 1).expand(B, S, h, D).to(torch.int8).contiguous()
+    k8 = (127 * sign(B * S * h)).view(B, S, h, 1).expand(B, S, h, D).to(torch.int8).contiguous()
+    # a few rows with mixed signs, so the dots also take values between the extremes
+    k8[:, ::7] = (127 * torch.randint(-1, 2, (B, len(range(0, S, 7)), h, D), generator=g)).to(torch.int8)
+    spad = (S + 63) // 64 * 64
+    codes = torch.randint(0, 256, (B, D, h, spad), generator=g, dtype=torch.int32)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                 # no NaN codes
+    codes[..., S:] = 0
+    v8 = codes.to(torch.uint8)
+    W = (S + 63) // 64
+    qs = torch.full((B, h, W), scale, dtype=torch.float32)
+    ks = torch.full((B, h, W), scale, dtype=torch.float32) * torch.linspace(0.5, 1.5, W)
+    say(f"[mfma consumer extremes] D={D} scale={scale}")
+    out = ulp.consumer_attention(*(t.to(DEV) for t in (q8, k8, v8, qs, ks)), used=S)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert torch.isfinite(out).all()
+    qsel = list(range(S))
+    for j in range(h):
+        xerr = mfma_exponent_error(qs, ks, 0, j, D)
+        ref, bound = consumer.fp8_probability_bound(q8, k8, v8, qs, ks, b=0, j=j, queries=qsel,
+                                                    used=S, exponent_error=xerr)
+        ratio = ((out[0, :, j].double() - ref).abs() / bound).max().item()
+        assert ratio <= 1.0, (D, scale, j, ratio)
