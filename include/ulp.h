@@ -333,8 +333,8 @@ int ulp_group_stats_with_mean(const void* q, const void* k, int dtype, int64_t B
  *   out[b,i,j,d] = sum_t softmax_t(score(i, .)) * e4m3(v8[b,d,j,t]) * (v_scale ? v_scale[b,j,d] : 1)
  * INT8 Q.K on MFMA (exact integer dot products); P quantized to E4M3 after scaling by 448
  * and P.V on FP8 MFMA with FP32 accumulation, so each probability carries a relative
- * rounding error of at most 2^-4 (absolute 2^-18 in the subnormal range).  Softmax
- * without a causal mask.
+ * rounding error of at most 2^-4 (absolute 2^-18 in the subnormal range); each row is
+ * normalized by the sum of its rounded probabilities.  Softmax without a causal mask.
  *   q8, k8     [B, S, h, D] int8;  v8 [B, D, h, Spad] E4M3 bytes, Spad = ceil(S/64)*64.
  *   q_scale, k_scale [B, h, W] float with W >= ceil(used/64); these two need only 4-byte
  *              alignment (a destination's slice of stacked scale tensors need not be
