@@ -73,6 +73,20 @@ MUTANTS = {
                        "return (uint16_t)(u >> 16);"),
     "bf16_ties_away": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);",
                        "return (uint16_t)((u + 0x8000u) >> 16);"),
+    "unpack_source_rank_interleaved": ("const uint8_t* chunk = recv + (t / L) * cb;",
+                                       "const uint8_t* chunk = recv + (t % P) * cb;"),
+    "unpack_k_from_q_section": ("k8[((b * S + t) * h + j) * D + d] = (int8_t)chunk[sec + src];",
+                                "k8[((b * S + t) * h + j) * D + d] = (int8_t)chunk[src];"),
+    "unpack_scale_width_floor": ("int64_t W = (ns + ORA_GROUP - 1) / ORA_GROUP;",
+                                 "int64_t W = ns / ORA_GROUP + (ns < ORA_GROUP);"),
+    "unpack_k_scale_section": ("memcpy(&kv, chunk + 3 * sec + ssec + 4 * ((b * h + j) * slots + sl), 4);",
+                               "memcpy(&kv, chunk + 3 * sec + 4 * ((b * h + j) * slots + sl), 4);"),
+    "unpack_scale_slot_shift": ("int64_t sl = g - first_group(s, L);",
+                                "int64_t sl = g - first_group(s, L) + (s > 0);"),
+    "pack_k_scale_from_q": ("ks[(b * h + j) * slots + sl] = k_amax[(b * H + hh) * slots + sl] / 127.0f;",
+                            "ks[(b * h + j) * slots + sl] = q_amax[(b * H + hh) * slots + sl] / 127.0f;"),
+    "pack_mean_local_head": ("float kc = elem(k, src, dtype) - elem(mean, (b * H + hh) * D + d, dtype);",
+                             "float kc = elem(k, src, dtype) - elem(mean, (b * H + j) * D + d, dtype);"),
 }
 
 
