@@ -85,6 +85,10 @@ MUTANTS = {
                                 "int64_t sl = g - first_group(s, L) + (s > 0);"),
     "pack_k_scale_from_q": ("ks[(b * h + j) * slots + sl] = k_amax[(b * H + hh) * slots + sl] / 127.0f;",
                             "ks[(b * h + j) * slots + sl] = q_amax[(b * H + hh) * slots + sl] / 127.0f;"),
+    "derive_mean_dropped": ("                        float m = mean ? elem(mean, (b * H + hh) * D + d, dtype) : 0.0f;\n                        float mn = gathered",
+                            "                        float m = 0.0f;\n                        float mn = gathered"),
+    "derive_last_toucher_only": ("best = fmaxf(best, c);", "best = c;"),
+    "quant_reciprocal_multiply": ("float q = rintf(x / scale);", "float q = rintf(x * (1.0f / scale));"),
     "pack_mean_local_head": ("float kc = elem(k, src, dtype) - elem(mean, (b * H + hh) * D + d, dtype);",
                              "float kc = elem(k, src, dtype) - elem(mean, (b * H + j) * D + d, dtype);"),
 }
