@@ -14,6 +14,7 @@ run a whole Ulysses group held by one GPU with one launch per step.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -126,6 +127,34 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+_F32 = (torch.float32,)
+_X16 = (torch.bfloat16, torch.float16)
+_I8 = (torch.int8,)
+_B8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _need(t, shape, dtypes, name):
+    """The library reads and writes every tensor by the sizes it is given, not by the
+    tensor's own: ``t`` (None passes) must hold exactly prod(shape) elements of one of
+    ``dtypes``, or the call is refused before anything runs."""
+    if t is None:
+        return
+    n = math.prod(shape)
+    if t.dtype not in dtypes or t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements {tuple(shape)} of "
+                         f"{'/'.join(str(d) for d in dtypes)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _need_bytes(t, nbytes, name):
+    """A byte buffer addressed by offsets the library computes (a destination stride may
+    reach past a view into the rest of its buffer): at least ``nbytes`` of the tensor's
+    storage from its first byte on."""
+    room = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if room < nbytes:
+        raise ValueError(f"{name} must reach at least {nbytes} bytes, its storage holds "
+                         f"{room} from its start")
+
+
 def _dt(t: torch.Tensor) -> int:
     if t.dtype not in _DTYPES:
         raise ValueError(f"expected bfloat16 or float16, got {t.dtype}")
@@ -152,6 +181,13 @@ def scale_widths(n: int) -> tuple[int, int]:
     return q.value, k.value
 
 
+def _need_unpack_out(out, shapes, lead=()):
+    qk, vs, sc = shapes
+    for t, shape, dts, name in zip(out, (qk, qk, vs, sc, sc), (_I8, _I8, _B8, _F32, _F32),
+                                   ("q8", "k8", "v8", "q_scale", "k_scale")):
+        _need(t, (*lead, *shape), dts, name)
+
+
 def unpack_shapes(batch_size, local_sequence, local_heads, head_dim, world_size,
                   scale_sequence=None):
     S = world_size * local_sequence
@@ -172,6 +208,8 @@ def k_grouped_amax(k, k_mean_global, *, rank, world_size, used_sequence=None, ou
     B, L, H, D = k.shape
     if out is None:
         out = torch.empty(B, H, slots(L), dtype=torch.float32, device=k.device)
+    _need(k_mean_global, (B, H, D), (k.dtype,), "k_mean_global")
+    _need(out, (B, H, slots(L)), _F32, "out")
     _check(lib().ulp_k_grouped_amax(_p(k), _p(k_mean_global), _dt(k), B, L, H, D, rank,
                                     world_size, _none(used_sequence), _p(out), _stream(k)))
     return out
@@ -183,6 +221,7 @@ def boundary_minmax(x, *, rank, world_size, used_sequence=None, out=None):
     B, L, H, D = x.shape
     if out is None:
         out = torch.empty(B, H, 2, 2, D, dtype=torch.float32, device=x.device)
+    _need(out, (B, H, 2, 2, D), _F32, "out")
     _check(lib().ulp_boundary_minmax(_p(x), _dt(x), B, L, H, D, rank, world_size,
                                      _none(used_sequence), _p(out), _stream(x)))
     return out
@@ -194,12 +233,22 @@ def derive_k_boundary_amax(grouped_amax, gathered_minmax, k_mean_global, *, rank
     flashinfer.comm._ulysses_lowp.derive_k_boundary_amax.  k_mean_global None: mean +0."""
     _dev(grouped_amax, gathered_minmax, k_mean_global)
     P, B, H, _, _, D = gathered_minmax.shape
+    _need(gathered_minmax, (world_size, B, H, 2, 2, D), _F32, "gathered_minmax")
+    _need(grouped_amax, (B, H, slots(local_sequence)), _F32, "grouped_amax")
+    _need(k_mean_global, (B, H, D), _X16, "k_mean_global")
     dt = _dt(k_mean_global) if k_mean_global is not None else 0
     _check(lib().ulp_derive_k_boundary_amax(_p(grouped_amax), _p(gathered_minmax),
                                             _p(k_mean_global), dt, B, H, D, rank,
                                             local_sequence, world_size,
                                             _stream(grouped_amax)))
     return grouped_amax
+
+
+def _need_shard_inputs(q, k, v, k_mean_global, B, L, H, D, lead=()):
+    """k and v like q (shape and dtype), the mean [B,H,D] in the same dtype."""
+    for t, name in ((k, "k"), (v, "v")):
+        _need(t, (*lead, B, L, H, D), (q.dtype,), name)
+    _need(k_mean_global, (B, H, D), (q.dtype,), "k_mean_global")
 
 
 def _v_scale(v_scale, B, H, D):
@@ -221,6 +270,10 @@ def pack(q, k, v, k_mean_global, q_amax, k_amax, *, rank, world_size, v_scale=No
     if send is None:
         send = torch.empty(world_size, cb, dtype=torch.uint8, device=q.device)
         dest_stride = cb
+    _need_shard_inputs(q, k, v, k_mean_global, B, L, H, D)
+    _need(q_amax, (B, H, slots(L)), _F32, "q_amax")
+    _need(k_amax, (B, H, slots(L)), _F32, "k_amax")
+    _need_bytes(send, (world_size - 1) * (dest_stride or cb) + cb, "send")
     _check(lib().ulp_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
                           _p(k_amax), _p(v_scale), B, L, H, D, rank, world_size, _p(send),
                           dest_stride or cb, _stream(q)))
@@ -246,6 +299,10 @@ def unpack_for_sage(recv_u8, *, batch_size, local_sequence, local_heads, head_di
                                                           local_heads, head_dim, world_size,
                                                           scale_sequence))
     _dev(recv_u8, *out)
+    _need_bytes(recv_u8, world_size * chunk_bytes(batch_size, local_sequence, local_heads,
+                                                  head_dim), "recv_u8")
+    _need_unpack_out(out, unpack_shapes(batch_size, local_sequence, local_heads, head_dim,
+                                        world_size, scale_sequence))
     q8, k8, v8, qs, ks = out
     _check(lib().ulp_unpack_for_sage(_p(recv_u8), batch_size, local_sequence, local_heads,
                                      head_dim, world_size, _none(aligned),
@@ -256,6 +313,18 @@ def unpack_for_sage(recv_u8, *, batch_size, local_sequence, local_heads, head_di
 
 # ------------------------------------------------------------------------- whole group
 
+def _need_group_stats(q, k, k_mean_global, out, world_size):
+    """Stacked shards [world_size,B,L,H,D]; statistics outputs of those sizes."""
+    P, B, L, H, D = q.shape
+    if P != world_size:
+        raise ValueError(f"stacked shards hold {P} ranks, world_size is {world_size}")
+    _need(k, q.shape, (q.dtype,), "k")
+    _need(k_mean_global, (B, H, D), (q.dtype,), "k_mean_global")
+    for t, shape, name in zip(out, ((P, B, H, slots(L)),) * 2 + ((P, B, H, 2, 2, D),) * 2,
+                              ("q_amax", "k_amax", "q_minmax", "k_minmax")):
+        _need(t, shape, _F32, name)
+
+
 def group_stats(q, k, k_mean_global, *, world_size, used_sequence=None, out=None):
     """Stacked shards [P,B,L,H,D] -> (q_amax, k_amax [P,B,H,slots], q_minmax, k_minmax
     [P,B,H,2,2,D]) in one launch."""
@@ -265,6 +334,7 @@ def group_stats(q, k, k_mean_global, *, world_size, used_sequence=None, out=None
         out = (torch.empty(P, B, H, slots(L), **f), torch.empty(P, B, H, slots(L), **f),
                torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f))
     _dev(q, k, k_mean_global, *out)
+    _need_group_stats(q, k, k_mean_global, out, world_size)
     qa, ka, qm, km = out
     _check(lib().ulp_group_stats(_p(q), _p(k), _p(k_mean_global), _dt(q), B, L, H, D,
                                  world_size, _none(used_sequence), _p(qa), _p(ka), _p(qm),
@@ -277,6 +347,11 @@ def group_derive(q_amax, k_amax, q_minmax, k_minmax, k_mean_global, *, local_seq
     """Boundary derive of every rank for Q and K, in place; returns (q_amax, k_amax)."""
     _dev(q_amax, k_amax, q_minmax, k_minmax, k_mean_global)
     P, B, H, _, _, D = k_minmax.shape
+    for t, name in ((q_minmax, "q_minmax"), (k_minmax, "k_minmax")):
+        _need(t, (world_size, B, H, 2, 2, D), _F32, name)
+    for t, name in ((q_amax, "q_amax"), (k_amax, "k_amax")):
+        _need(t, (world_size, B, H, slots(local_sequence)), _F32, name)
+    _need(k_mean_global, (B, H, D), _X16, "k_mean_global")
     _check(lib().ulp_group_derive(_p(q_amax), _p(k_amax), _p(q_minmax), _p(k_minmax),
                                   _p(k_mean_global), _dt(k_mean_global), B, H, D,
                                   local_sequence, world_size, _stream(q_amax)))
@@ -297,6 +372,12 @@ def group_pack(q, k, v, k_mean_global, q_amax, k_amax, *, world_size, v_scale=No
         group = group_buffer(B, L, H, D, world_size, q.device)
     _dev(q, k, v, k_mean_global, q_amax, k_amax, v_scale, group)
     _v_scale(v_scale, B, H, D)
+    if P != world_size:
+        raise ValueError(f"stacked shards hold {P} ranks, world_size is {world_size}")
+    _need_shard_inputs(q, k, v, k_mean_global, B, L, H, D, lead=(P,))
+    _need(q_amax, (P, B, H, slots(L)), _F32, "q_amax")
+    _need(k_amax, (P, B, H, slots(L)), _F32, "k_amax")
+    _need_bytes(group, P * P * chunk_bytes(B, L, H // world_size, D), "group")
     _check(lib().ulp_group_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(q_amax),
                                 _p(k_amax), _p(v_scale), B, L, H, D, world_size, _p(group),
                                 _stream(q)))
@@ -311,6 +392,10 @@ def group_unpack(group, *, batch_size, local_sequence, local_heads, head_dim, wo
                                                         local_heads, head_dim, world_size,
                                                         scale_sequence), lead=(world_size,))
     _dev(group, *out)
+    _need_bytes(group, world_size * world_size * chunk_bytes(batch_size, local_sequence,
+                                                              local_heads, head_dim), "group")
+    _need_unpack_out(out, unpack_shapes(batch_size, local_sequence, local_heads, head_dim,
+                                        world_size, scale_sequence), lead=(world_size,))
     q8, k8, v8, qs, ks = out
     _check(lib().ulp_group_unpack(_p(group), batch_size, local_sequence, local_heads,
                                   head_dim, world_size, _none(aligned), _none(scale_sequence),
@@ -341,6 +426,11 @@ def stats_pack(q, k, v, k_mean_global, *, rank, world_size, used_sequence=None, 
         dest_stride = cb
     _dev(q, k, v, k_mean_global, v_scale, *out)
     _v_scale(v_scale, B, H, D)
+    _need_shard_inputs(q, k, v, k_mean_global, B, L, H, D)
+    for t, shape, name in zip(out, ((B, H, slots(L)),) * 2 + ((B, H, 2, 2, D),) * 2,
+                              ("q_amax", "k_amax", "q_minmax", "k_minmax")):
+        _need(t, shape, _F32, name)
+    _need_bytes(send, (world_size - 1) * (dest_stride or cb) + cb, "send")
     qa, ka, qm, km = out
     _check(lib().ulp_stats_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q), _p(v_scale),
                                 B, L, H, D, rank, world_size, _none(used_sequence), _p(qa),
@@ -353,9 +443,16 @@ def derive_pack(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, *, rank
                 send, used_sequence=None, dest_stride=None):
     """derive_k_boundary_amax on both amax in place (gathered min/max [P,B,H,2,2,D]), then
     the pack of the slots that waited for it.  Returns (q_amax, k_amax)."""
-    _dev(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax)
+    _dev(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, send)
     B, L, H, D = q.shape
     cb = chunk_bytes(B, L, H // world_size, D)
+    _need(k, (B, L, H, D), (q.dtype,), "k")
+    _need(k_mean_global, (B, H, D), (q.dtype,), "k_mean_global")
+    for t, name in ((q_amax, "q_amax"), (k_amax, "k_amax")):
+        _need(t, (B, H, slots(L)), _F32, name)
+    for t, name in ((q_minmax, "q_minmax"), (k_minmax, "k_minmax")):
+        _need(t, (world_size, B, H, 2, 2, D), _F32, name)
+    _need_bytes(send, (world_size - 1) * (dest_stride or cb) + cb, "send")
     _check(lib().ulp_derive_pack(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
                                  _p(k_amax), _p(q_minmax), _p(k_minmax), B, L, H, D, rank,
                                  world_size, _none(used_sequence), _p(send), dest_stride or cb,
@@ -374,6 +471,9 @@ def group_stats_pack(q, k, v, k_mean_global, *, world_size, used_sequence=None, 
         group = group_buffer(B, L, H, D, world_size, q.device)
     _dev(q, k, v, k_mean_global, v_scale, group, *out)
     _v_scale(v_scale, B, H, D)
+    _need_group_stats(q, k, k_mean_global, out, world_size)
+    _need(v, q.shape, (q.dtype,), "v")
+    _need_bytes(group, P * P * chunk_bytes(B, L, H // world_size, D), "group")
     qa, ka, qm, km = out
     _check(lib().ulp_group_stats_pack(_p(q), _p(k), _p(v), _p(k_mean_global), _dt(q),
                                       _p(v_scale), B, L, H, D, world_size,
@@ -387,6 +487,8 @@ def group_derive_pack(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, *
     """derive_pack for every rank (after group_stats_pack); returns (q_amax, k_amax)."""
     _dev(q, k, k_mean_global, q_amax, k_amax, q_minmax, k_minmax, group)
     P, B, L, H, D = q.shape
+    _need_group_stats(q, k, k_mean_global, (q_amax, k_amax, q_minmax, k_minmax), world_size)
+    _need_bytes(group, P * P * chunk_bytes(B, L, H // world_size, D), "group")
     _check(lib().ulp_group_derive_pack(_p(q), _p(k), _p(k_mean_global), _dt(q), _p(q_amax),
                                        _p(k_amax), _p(q_minmax), _p(k_minmax), B, L, H, D,
                                        world_size, _none(used_sequence), _p(group),
@@ -408,6 +510,10 @@ def k_mean(k, *, world_size, used_sequence=None, workspace=None, out=None):
                torch.empty(B, H, D, dtype=k.dtype, device=k.device))
     _dev(k, workspace, *out)
     mf, md = out
+    if P != world_size:
+        raise ValueError(f"stacked shards hold {P} ranks, world_size is {world_size}")
+    _need(mf, (B, H, D), _F32, "mean_f32")
+    _need(md, (B, H, D), (k.dtype,), "mean_dtype")
     _check(lib().ulp_k_mean(_p(k), _dt(k), B, L, H, D, world_size, _none(used_sequence),
                             _p(workspace), workspace.numel() * workspace.element_size(),
                             _p(mf), _p(md), _stream(k)))
@@ -421,6 +527,10 @@ def k_mean_noalloc(k, *, world_size, out, used_sequence=None):
     P, B, L, H, D = k.shape
     mf, md = out
     _dev(k, mf, md)
+    if P != world_size:
+        raise ValueError(f"stacked shards hold {P} ranks, world_size is {world_size}")
+    _need(mf, (B, H, D), _F32, "mean_f32")
+    _need(md, (B, H, D), (k.dtype,), "mean_dtype")
     _check(lib().ulp_k_mean_noalloc(_p(k), _dt(k), B, L, H, D, world_size,
                                     _none(used_sequence), _p(mf), _p(md), _stream(k)))
     return mf, md
@@ -440,6 +550,9 @@ def group_stats_with_mean(q, k, *, world_size, used_sequence=None, workspace=Non
                torch.empty(P, B, H, 2, 2, D, **f), torch.empty(P, B, H, 2, 2, D, **f),
                torch.empty(B, H, D, **f), torch.empty(B, H, D, dtype=q.dtype, device=q.device))
     _dev(q, k, workspace, *out)
+    _need_group_stats(q, k, None, out[:4], world_size)
+    _need(out[4], (B, H, D), _F32, "mean_f32")
+    _need(out[5], (B, H, D), (q.dtype,), "mean_dtype")
     qa, ka, qm, km, mf, md = out
     _check(lib().ulp_group_stats_with_mean(
         _p(q), _p(k), _dt(q), B, L, H, D, world_size, _none(used_sequence), _p(workspace),
@@ -462,6 +575,14 @@ def consumer_attention(q8, k8, v8, q_scale, k_scale, *, used, v_scale=None, out=
     if out is None:
         out = torch.empty(B, used, h, D, dtype=torch.float32, device=q8.device)
     _dev(q8, k8, v8, q_scale, k_scale, v_scale, out)
+    _need(q8, (B, S, h, D), _I8, "q8")
+    _need(k8, (B, S, h, D), _I8, "k8")
+    _need(v8, (B, D, h, (S + GROUP_ROWS - 1) // GROUP_ROWS * GROUP_ROWS), _B8, "v8")
+    _need(q_scale, (B, h, W), _F32, "q_scale")
+    _need(k_scale, (B, h, W), _F32, "k_scale")
+    if not 1 <= used <= S:
+        raise ValueError(f"used must be in [1, {S}], got {used}")
+    _need(out, (B, used, h, D), _F32, "out")
     _check(lib().ulp_consumer_attention(_p(q8), _p(k8), _p(v8), _p(q_scale), _p(k_scale),
                                         _p(v_scale), B, S, h, D, W, used, _p(out),
                                         _stream(q8)))
