@@ -243,3 +243,29 @@ def test_mfma_consumer_extreme_dot_products(olib, D, scale):
                                                     used=S, exponent_error=xerr)
         ratio = ((out[0, :, j].double() - ref).abs() / bound).max().item()
         assert ratio <= 1.0, (D, scale, j, ratio)
+
+
+def _random_geometries(n, seed=2024):
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for _ in range(n):
+        P = [2, 4, 8][int(torch.randint(0, 3, (1,), generator=g))]
+        L = int(torch.randint(1, 400, (1,), generator=g))
+        D = [64, 128][int(torch.randint(0, 2, (1,), generator=g))]
+        H = P * int(torch.randint(1, 4, (1,), generator=g))
+        S = P * L
+        used = int(torch.randint(1, S + 1, (1,), generator=g))
+        dtype = [torch.bfloat16, torch.float16][int(torch.randint(0, 2, (1,), generator=g))]
+        out.append((P, L, H, D, used, dtype))
+    return out
+
+
+@pytest.mark.parametrize("P,L,H,D,used,dtype", _random_geometries(10))
+def test_mfma_consumer_random_geometries(olib, P, L, H, D, used, dtype):
+    """Seeded random world sizes, shard lengths, head counts, head dims, live prefixes and
+    dtypes: every element of every destination and head within the FP8 bound."""
+    w, d = grouped_inputs(small(B=1, P=P, L=L, H=H, D=D, dtype=dtype, used=used,
+                                scale_sequence=used, seed=P * 1000 + L))
+    vs = caller_v_scale(d, w) if dtype == torch.float16 else None
+    g = run_group(w, to_dev(d, w.P), v_scale=None if vs is None else vs.to(DEV))
+    _check_mfma_consumer(w, d, g, vs, range(w.P), lambda p: range(w.h), 32, w.name)
